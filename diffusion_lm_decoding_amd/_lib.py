@@ -1,0 +1,115 @@
+"""ctypes binding of libdllm.so (the C ABI declared in include/dllm.h).
+
+Argument marshalling only: every step of the decode runs in the HIP library.
+Loading fails loudly when the library has not been built; there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdllm.so")
+
+OK, ERR_ARG, ERR_OOM, ERR_DEVICE, ERR_STATE, ERR_NUMERIC = range(6)
+STATUS_NAMES = {0: "OK", 1: "ERR_ARG", 2: "ERR_OOM", 3: "ERR_DEVICE", 4: "ERR_STATE", 5: "ERR_NUMERIC"}
+F32, BF16 = 0, 1
+CACHE = {"none": 0, "prefix": 1, "dual": 2, "block_causal": 3}
+RULE = {"threshold": 0, "factor": 1, "topk": 2}
+
+SYMBOLS = ("dllm_init_weights", "dllm_refresh_cache", "dllm_block_step", "dllm_decode",
+           "dllm_destroy", "dllm_last_error")
+
+
+class ModelCfg(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("d_model", C.c_int32), ("n_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("d_ffn", C.c_int32), ("vocab", C.c_int32),
+                ("mask_id", C.c_int32), ("rms_eps", C.c_float), ("rope_theta", C.c_float),
+                ("dtype", C.c_int32), ("max_batch", C.c_int32), ("max_seq", C.c_int32)]
+
+
+class DecodeCfg(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("prompt_len", C.c_int32), ("gen_len", C.c_int32),
+                ("block_len", C.c_int32), ("cache", C.c_int32), ("rule", C.c_int32),
+                ("tau", C.c_float), ("factor", C.c_float), ("k", C.c_int32),
+                ("refresh_every", C.c_int32)]
+
+
+class Canvas(C.Structure):
+    _fields_ = [("tokens", C.c_void_p), ("bias_target", C.c_void_p), ("bias_alpha", C.c_void_p),
+                ("commit_step", C.c_void_p)]
+
+
+class Stats(C.Structure):
+    _fields_ = [("steps", C.c_int64), ("refreshes", C.c_int64), ("committed", C.c_int64),
+                ("max_seq_steps", C.c_int64), ("ms_total", C.c_double), ("ms_refresh", C.c_double)]
+
+
+class DllmError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> C.CDLL:
+    """Load libdllm.so once; raise if it is missing (no CPU fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m diffusion_lm_decoding_amd.build`")
+    lib = C.CDLL(path)
+    P = C.c_void_p
+    lib.dllm_init_weights.argtypes = [C.POINTER(P), C.POINTER(ModelCfg), C.POINTER(P), P]
+    lib.dllm_init_weights.restype = C.c_int
+    lib.dllm_refresh_cache.argtypes = [P, C.POINTER(Canvas), C.POINTER(DecodeCfg), C.c_int32]
+    lib.dllm_refresh_cache.restype = C.c_int
+    lib.dllm_block_step.argtypes = [P, C.POINTER(Canvas), C.POINTER(DecodeCfg), C.c_int32,
+                                    C.POINTER(C.c_int32), C.POINTER(C.c_int32), P, P, P]
+    lib.dllm_block_step.restype = C.c_int
+    lib.dllm_decode.argtypes = [P, C.POINTER(Canvas), C.POINTER(DecodeCfg), C.POINTER(Stats)]
+    lib.dllm_decode.restype = C.c_int
+    lib.dllm_destroy.argtypes = [P]
+    lib.dllm_destroy.restype = None
+    lib.dllm_last_error.argtypes = []
+    lib.dllm_last_error.restype = C.c_char_p
+    _lib = lib
+    return lib
+
+
+def check(status: int) -> None:
+    if status != OK:
+        raise DllmError(status, load().dllm_last_error().decode())
+
+
+def dllm_init_weights(cfg: ModelCfg, tensor_ptrs, stream_ptr: int) -> int:
+    lib = load()
+    arr = (C.c_void_p * len(tensor_ptrs))(*tensor_ptrs)
+    out = C.c_void_p()
+    check(lib.dllm_init_weights(C.byref(out), C.byref(cfg), arr, C.c_void_p(stream_ptr)))
+    return out.value
+
+
+def dllm_refresh_cache(ctx: int, canvas: Canvas, cfg: DecodeCfg, block_idx: int) -> None:
+    check(load().dllm_refresh_cache(C.c_void_p(ctx), C.byref(canvas), C.byref(cfg), block_idx))
+
+
+def dllm_block_step(ctx: int, canvas: Canvas, cfg: DecodeCfg, block_idx: int, n_committed=None,
+                    block_done=None, dbg_logits=0, dbg_conf=0, dbg_tok=0) -> None:
+    check(load().dllm_block_step(C.c_void_p(ctx), C.byref(canvas), C.byref(cfg), block_idx,
+                                 n_committed, block_done, C.c_void_p(dbg_logits),
+                                 C.c_void_p(dbg_conf), C.c_void_p(dbg_tok)))
+
+
+def dllm_decode(ctx: int, canvas: Canvas, cfg: DecodeCfg) -> Stats:
+    st = Stats()
+    check(load().dllm_decode(C.c_void_p(ctx), C.byref(canvas), C.byref(cfg), C.byref(st)))
+    return st
+
+
+def dllm_destroy(ctx: int) -> None:
+    load().dllm_destroy(C.c_void_p(ctx))

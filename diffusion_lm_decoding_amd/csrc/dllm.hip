@@ -1,0 +1,611 @@
+// Engine behind the C ABI in include/dllm.h: context and weight packing, the
+// model forward over a set of canvas rows, the block step, the cache passes
+// and the host block loop (Fast-dLLM reading notes, Algorithm 1).
+#include <hip/hip_runtime.h>
+
+#include <chrono>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/dllm.h"
+#include "attention.h"
+#include "gemm.h"
+#include "ops.h"
+
+using namespace dllm;
+
+namespace {
+
+thread_local std::string g_err;
+
+dllm_status fail(dllm_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+#define HIPCHK(call)                                                                          \
+  do {                                                                                        \
+    hipError_t e_ = (call);                                                                   \
+    if (e_ != hipSuccess)                                                                     \
+      return fail(DLLM_ERR_DEVICE, std::string(#call) + ": " + hipGetErrorString(e_));        \
+  } while (0)
+
+#define TRY(call)                         \
+  do {                                    \
+    dllm_status s_ = (call);              \
+    if (s_ != DLLM_OK) return s_;         \
+  } while (0)
+
+constexpr int kMaxBlock = 256;      // select/commit handles a block in one workgroup
+constexpr int kTargetWGs = 512;     // aim for >= 2 workgroups per CU
+
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+struct dllm_ctx {
+  dllm_model_cfg cfg{};
+  hipStream_t stream = nullptr;
+  bool bf16 = true;
+  int esz = 2;
+  int seq_pad = 0;
+  int max_rows = 0, max_rows_pad = 0, max_head = 0, max_head_pad = 0;
+  int n_vtiles = 0;
+
+  std::vector<void*> allocs;
+  void* emb = nullptr;
+  std::vector<float*> g_attn, g_ffn;
+  float* g_final = nullptr;
+  std::vector<void*> wqkv, wo, wgu, wd;
+  void* wlm = nullptr;
+  float* rope_cos = nullptr;
+  float* rope_sin = nullptr;
+  void* kc = nullptr;
+  void* vt = nullptr;
+  size_t kv_layer = 0;  // elements per layer
+
+  float* x = nullptr;
+  void* xin = nullptr;
+  void* q = nullptr;
+  void* attn_out = nullptr;
+  void* act = nullptr;
+  void* xh = nullptr;
+  float* pmax = nullptr;
+  float* psum = nullptr;
+  int* parg = nullptr;
+  float* conf = nullptr;
+  int* tok = nullptr;
+  float* gemm_ws = nullptr;
+  size_t gemm_ws_floats = 0;
+  unsigned* counters = nullptr;
+  size_t n_counters = 0;
+  float* attn_ws = nullptr;
+  size_t attn_ws_floats = 0;
+  unsigned* attn_counters = nullptr;
+  size_t n_attn_counters = 0;
+
+  int* d_err = nullptr;       // [0] numeric error, [1] canvas check
+  int* d_ncommit = nullptr;   // [max_batch]
+  int* d_done = nullptr;
+  int* d_step = nullptr;
+  int* h_pin = nullptr;       // pinned: ncommit[max_batch], done[max_batch], err[2]
+
+  ~dllm_ctx() {
+    for (void* p : allocs) (void)hipFree(p);
+    if (h_pin) (void)hipHostFree(h_pin);
+  }
+
+  template <typename P>
+  dllm_status alloc(P** out, size_t bytes) {
+    void* p = nullptr;
+    bytes = bytes ? bytes : 16;
+    if (hipMalloc(&p, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(DLLM_ERR_OOM, "hipMalloc of " + std::to_string(bytes) + " bytes failed");
+    }
+    allocs.push_back(p);
+    if (hipMemsetAsync(p, 0, bytes, stream) != hipSuccess) return fail(DLLM_ERR_DEVICE, "hipMemsetAsync failed");
+    *out = static_cast<P*>(p);
+    return DLLM_OK;
+  }
+};
+
+namespace {
+
+dllm_status check_launch() {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DLLM_ERR_DEVICE, std::string("kernel launch: ") + hipGetErrorString(e));
+  return DLLM_OK;
+}
+
+dllm_status validate_model(const dllm_model_cfg* c) {
+  if (!c) return fail(DLLM_ERR_ARG, "cfg is NULL");
+  if (c->dtype != DLLM_F32 && c->dtype != DLLM_BF16) return fail(DLLM_ERR_ARG, "dtype must be DLLM_F32 or DLLM_BF16");
+  if (c->n_layers < 1 || c->n_heads < 1) return fail(DLLM_ERR_ARG, "n_layers and n_heads must be >= 1");
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
+    return fail(DLLM_ERR_ARG, "head_dim must be 32, 64 or 128");
+  if (c->d_model != c->n_heads * c->head_dim) return fail(DLLM_ERR_ARG, "d_model must equal n_heads*head_dim");
+  if (c->d_model % 32 || c->d_ffn % 32 || c->vocab % 32 || c->d_ffn < 32 || c->vocab < 64)
+    return fail(DLLM_ERR_ARG, "d_model, d_ffn and vocab must be positive multiples of 32");
+  if (c->mask_id < 0 || c->mask_id >= c->vocab) return fail(DLLM_ERR_ARG, "mask_id out of range");
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 1.f)) return fail(DLLM_ERR_ARG, "rms_eps > 0 and rope_theta > 1 required");
+  if (c->max_batch < 1 || c->max_seq < 2) return fail(DLLM_ERR_ARG, "max_batch >= 1 and max_seq >= 2 required");
+  if ((long long)c->max_batch * c->max_seq > (1LL << 26)) return fail(DLLM_ERR_ARG, "max_batch*max_seq too large");
+  return DLLM_OK;
+}
+
+dllm_status validate_decode(const dllm_ctx* ctx, const dllm_decode_cfg* d) {
+  if (!d) return fail(DLLM_ERR_ARG, "decode cfg is NULL");
+  if (d->batch < 1 || d->batch > ctx->cfg.max_batch) return fail(DLLM_ERR_ARG, "batch out of range [1, max_batch]");
+  if (d->prompt_len < 1 || d->gen_len < 1 || d->block_len < 1) return fail(DLLM_ERR_ARG, "prompt_len, gen_len, block_len must be >= 1");
+  if (d->gen_len % d->block_len) return fail(DLLM_ERR_ARG, "gen_len must be a multiple of block_len");
+  if (d->block_len > kMaxBlock) return fail(DLLM_ERR_ARG, "block_len must be <= 256");
+  if (d->prompt_len + d->gen_len > ctx->cfg.max_seq) return fail(DLLM_ERR_ARG, "prompt_len + gen_len exceeds max_seq");
+  if (d->cache < DLLM_CACHE_NONE || d->cache > DLLM_CACHE_BLOCK_CAUSAL) return fail(DLLM_ERR_ARG, "unknown cache mode");
+  if (d->rule < DLLM_RULE_THRESHOLD || d->rule > DLLM_RULE_TOPK) return fail(DLLM_ERR_ARG, "unknown rule");
+  if (d->rule == DLLM_RULE_THRESHOLD && !(d->tau > 0.f && d->tau <= 1.f)) return fail(DLLM_ERR_ARG, "tau must be in (0, 1]");
+  if (d->rule == DLLM_RULE_FACTOR && !(d->factor > 0.f)) return fail(DLLM_ERR_ARG, "factor must be > 0");
+  if (d->rule == DLLM_RULE_TOPK && d->k < 1) return fail(DLLM_ERR_ARG, "k must be >= 1");
+  if (d->refresh_every < 0) return fail(DLLM_ERR_ARG, "refresh_every must be >= 0");
+  return DLLM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// launch helpers
+// ---------------------------------------------------------------------------
+template <typename T, int MT, class Epi>
+dllm_status launch_gemm_mt(dllm_ctx* c, const void* X, const void* W, int M, int N, int K, const Epi& epi) {
+  GemmArgs a{};
+  a.X = static_cast<const Frag16*>(X);
+  a.W = static_cast<const Frag16*>(W);
+  a.KT = K / Mfma<T>::KF;
+  a.n_tiles = N / 32;
+  a.m_tiles = cdiv(M, 32);
+  a.m_groups = cdiv(a.m_tiles, MT);
+  const long base = (long)a.n_tiles * a.m_groups;
+  int splits = 1;
+  // split K until the grid fills the chip; keep >= 8 fragments per wave
+  while (base * splits < kTargetWGs && a.KT / (splits * 2 * 4) >= 8) splits *= 2;
+  while (splits > 1 && ((size_t)splits * base * MT * 1024 > c->gemm_ws_floats || (size_t)base > c->n_counters))
+    splits /= 2;
+  a.splits = splits;
+  a.ws = c->gemm_ws;
+  a.counters = c->counters;
+  hipLaunchKernelGGL((gemm_stream_kernel<T, MT, Epi>), dim3((unsigned)(base * splits)), dim3(256), 0, c->stream, a, epi);
+  return check_launch();
+}
+
+template <typename T, class Epi>
+dllm_status launch_gemm(dllm_ctx* c, const void* X, const void* W, int M, int N, int K, const Epi& epi) {
+  const int mt = cdiv(M, 32);
+  if (mt <= 1) return launch_gemm_mt<T, 1>(c, X, W, M, N, K, epi);
+  if (mt <= 2) return launch_gemm_mt<T, 2>(c, X, W, M, N, K, epi);
+  return launch_gemm_mt<T, 4>(c, X, W, M, N, K, epi);
+}
+
+struct Fwd {
+  const int* tokens;
+  int seq_len;          // canvas row length
+  int batch, nr, row_start;
+  int N, P, blk, block_causal;
+  bool kv_only;         // last layer: K/V only (cache passes)
+};
+
+template <typename T, int DH>
+dllm_status launch_attn(dllm_ctx* c, int layer, const Fwd& f) {
+  const dllm_model_cfg& m = c->cfg;
+  AttnArgs a{};
+  a.q = c->q;
+  a.kc = static_cast<const T*>(c->kc) + (size_t)layer * c->kv_layer;
+  a.vt = static_cast<const T*>(c->vt) + (size_t)layer * c->kv_layer;
+  a.out = c->attn_out;
+  a.g = RowGeom{f.batch * f.nr, f.nr, f.row_start};
+  a.H = m.n_heads;
+  a.d = m.d_model;
+  a.seq_pad = c->seq_pad;
+  a.N = f.N;
+  a.P = f.P;
+  a.blk = f.blk;
+  a.block_causal = f.block_causal;
+  a.qblocks = cdiv(f.nr, 32);
+  const int nwg = f.batch * m.n_heads * a.qblocks;
+  const int ntile = cdiv(f.N, 32);
+  int splits = 1;
+  while (nwg * splits < kTargetWGs && ntile / (splits * 2) >= 8) splits *= 2;
+  const size_t rec = (size_t)(DH / 32 * 16 + 2) * 64;
+  while (splits > 1 && ((size_t)splits * nwg * rec > c->attn_ws_floats || (size_t)nwg > c->n_attn_counters))
+    splits /= 2;
+  a.splits = splits;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)DH));
+  a.ws = c->attn_ws;
+  a.counters = c->attn_counters;
+  hipLaunchKernelGGL((attn_kernel<T, DH>), dim3(nwg, splits), dim3(256), 0, c->stream, a);
+  return check_launch();
+}
+
+template <typename T>
+dllm_status attention(dllm_ctx* c, int layer, const Fwd& f) {
+  switch (c->cfg.head_dim) {
+    case 32: return launch_attn<T, 32>(c, layer, f);
+    case 64: return launch_attn<T, 64>(c, layer, f);
+    default: return launch_attn<T, 128>(c, layer, f);
+  }
+}
+
+template <typename T>
+dllm_status rmsnorm(dllm_ctx* c, int rows, int blk, int src_nr, int src_off, const float* gain, void* out) {
+  hipLaunchKernelGGL((rmsnorm_pack_kernel<T>), dim3(rows), dim3(256), 0, c->stream, c->x, c->cfg.d_model, blk,
+                     src_nr, src_off, gain, c->cfg.rms_eps, static_cast<T*>(out));
+  return check_launch();
+}
+
+// Model forward over rows [row_start, row_start + nr) of every sequence.
+template <typename T>
+dllm_status forward(dllm_ctx* c, const Fwd& f) {
+  const dllm_model_cfg& m = c->cfg;
+  const int M = f.batch * f.nr, d = m.d_model, F = m.d_ffn;
+  const RowGeom g{M, f.nr, f.row_start};
+  hipLaunchKernelGGL((embed_kernel<T>), dim3(M), dim3(256), 0, c->stream, f.tokens, f.seq_len, g,
+                     static_cast<const T*>(c->emb), d, m.vocab, c->x);
+  TRY(check_launch());
+  for (int l = 0; l < m.n_layers; ++l) {
+    TRY(rmsnorm<T>(c, M, M, M, 0, c->g_attn[l], c->xin));
+    EpiQKV<T> eq{g, d, m.head_dim, m.n_heads, c->seq_pad, static_cast<T*>(c->q),
+                 static_cast<T*>(c->kc) + (size_t)l * c->kv_layer, static_cast<T*>(c->vt) + (size_t)l * c->kv_layer,
+                 c->rope_cos, c->rope_sin};
+    TRY(launch_gemm<T>(c, c->xin, c->wqkv[l], M, 3 * d, d, eq));
+    if (f.kv_only && l == m.n_layers - 1) break;
+    TRY(attention<T>(c, l, f));
+    TRY(launch_gemm<T>(c, c->attn_out, c->wo[l], M, d, d, EpiResidual{M, d, c->x}));
+    TRY(rmsnorm<T>(c, M, M, M, 0, c->g_ffn[l], c->xin));
+    TRY(launch_gemm<T>(c, c->xin, c->wgu[l], M, 2 * F, d, EpiSwiGLU<T>{M, F, static_cast<T*>(c->act)}));
+    TRY(launch_gemm<T>(c, c->act, c->wd[l], M, d, F, EpiResidual{M, d, c->x}));
+  }
+  return DLLM_OK;
+}
+
+Fwd make_fwd(const dllm_ctx* c, const dllm_canvas* cv, const dllm_decode_cfg* d) {
+  (void)c;
+  Fwd f{};
+  f.tokens = cv->tokens;
+  f.seq_len = d->prompt_len + d->gen_len;
+  f.batch = d->batch;
+  f.N = f.seq_len;
+  f.P = d->prompt_len;
+  f.blk = d->block_len;
+  f.block_causal = d->cache == DLLM_CACHE_BLOCK_CAUSAL;
+  f.kv_only = false;
+  return f;
+}
+
+template <typename T>
+dllm_status refresh_impl(dllm_ctx* c, const dllm_canvas* cv, const dllm_decode_cfg* d, int block_idx) {
+  Fwd f = make_fwd(c, cv, d);
+  f.kv_only = true;
+  if (d->cache == DLLM_CACHE_BLOCK_CAUSAL) {
+    if (block_idx < 0) {
+      f.row_start = 0;
+      f.nr = d->prompt_len;
+    } else {
+      if (block_idx >= d->gen_len / d->block_len) return fail(DLLM_ERR_ARG, "block_idx out of range");
+      f.row_start = d->prompt_len + block_idx * d->block_len;
+      f.nr = d->block_len;
+    }
+  } else {
+    f.row_start = 0;
+    f.nr = f.seq_len;
+  }
+  return forward<T>(c, f);
+}
+
+template <typename T>
+dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, int j, int* n_committed,
+                      int* block_done, float* dbg_logits, float* dbg_conf, int* dbg_tok) {
+  const dllm_model_cfg& m = c->cfg;
+  if (j < 0 || j >= d->gen_len / d->block_len) return fail(DLLM_ERR_ARG, "block_idx out of range");
+  Fwd f = make_fwd(c, cv, d);
+  const int s = d->prompt_len + j * d->block_len;
+  switch (d->cache) {
+    case DLLM_CACHE_NONE: f.row_start = 0; f.nr = f.seq_len; break;
+    case DLLM_CACHE_PREFIX: f.row_start = s; f.nr = f.seq_len - s; break;
+    default: f.row_start = s; f.nr = d->block_len; break;
+  }
+  TRY(forward<T>(c, f));
+  const int B = d->block_len, HR = d->batch * B;
+  // final norm of the block rows, then LM head -> (max, sum, argmax) partials
+  TRY(rmsnorm<T>(c, HR, B, f.nr, s - f.row_start, c->g_final, c->xh));
+  EpiLMHead eh{HR, B, d->gen_len, s - d->prompt_len, cv->bias_target, cv->bias_alpha, m.mask_id, m.vocab,
+               c->pmax, c->psum, c->parg, dbg_logits};
+  if ((cv->bias_target == nullptr) != (cv->bias_alpha == nullptr)) return fail(DLLM_ERR_ARG, "bias_target and bias_alpha must both be set or both NULL");
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, c->stream, c->d_err, 2, 0);
+  TRY(check_launch());
+  TRY(launch_gemm<T>(c, c->xh, c->wlm, HR, m.vocab, m.d_model, eh));
+  hipLaunchKernelGGL(lm_merge_kernel, dim3(HR), dim3(256), 0, c->stream, c->pmax, c->psum, c->parg, c->n_vtiles, HR,
+                     c->conf, c->tok, c->d_err);
+  TRY(check_launch());
+  SelectArgs sa{};
+  sa.tokens = cv->tokens;
+  sa.seq_len = f.seq_len;
+  sa.prompt_len = d->prompt_len;
+  sa.gen_len = d->gen_len;
+  sa.blk = B;
+  sa.start = s;
+  sa.mask_id = m.mask_id;
+  sa.conf = c->conf;
+  sa.tok = c->tok;
+  sa.rule = d->rule;
+  sa.tau = d->tau;
+  sa.factor = d->factor;
+  sa.k = d->k;
+  sa.step_ctr = c->d_step;
+  sa.commit_step = cv->commit_step;
+  sa.ncommit = c->d_ncommit;
+  sa.done = c->d_done;
+  sa.err = c->d_err;
+  sa.dbg_conf = dbg_conf;
+  sa.dbg_tok = dbg_tok;
+  hipLaunchKernelGGL(select_commit_kernel, dim3(d->batch), dim3(256), 0, c->stream, sa);
+  TRY(check_launch());
+  const int mb = c->cfg.max_batch;
+  HIPCHK(hipMemcpyAsync(c->h_pin, c->d_ncommit, d->batch * sizeof(int), hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(hipMemcpyAsync(c->h_pin + mb, c->d_done, d->batch * sizeof(int), hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(hipMemcpyAsync(c->h_pin + 2 * mb, c->d_err, sizeof(int), hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(hipStreamSynchronize(c->stream));
+  if (c->h_pin[2 * mb]) return fail(DLLM_ERR_NUMERIC, "non-finite logits or confidence in the LM head");
+  for (int b = 0; b < d->batch; ++b) {
+    if (n_committed) n_committed[b] = c->h_pin[b];
+    if (block_done) block_done[b] = c->h_pin[mb + b];
+  }
+  return DLLM_OK;
+}
+
+template <typename T>
+dllm_status pack(dllm_ctx* c, const void* src, const void* src2, int rows, int K, int mode, void* dst, int row0) {
+  const size_t n = (size_t)rows * K;
+  hipLaunchKernelGGL((pack_kernel<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, c->stream,
+                     static_cast<const T*>(src), static_cast<const T*>(src2), rows, K, mode, c->cfg.head_dim,
+                     static_cast<T*>(dst), row0);
+  return check_launch();
+}
+
+template <typename T>
+dllm_status init_impl(dllm_ctx* c, const void* const* t) {
+  const dllm_model_cfg& m = c->cfg;
+  const int d = m.d_model, F = m.d_ffn, V = m.vocab, L = m.n_layers, dh = m.head_dim;
+  const size_t es = sizeof(T);
+  for (int i = 0; i < 2 + 9 * L; ++i)
+    if (!t[i]) return fail(DLLM_ERR_ARG, "tensor pointer " + std::to_string(i) + " is NULL");
+  auto gain = [&](const void* src, float** out) -> dllm_status {
+    TRY(c->alloc(out, (size_t)d * sizeof(float)));
+    hipLaunchKernelGGL((to_f32_kernel<T>), dim3(cdiv(d, 256)), dim3(256), 0, c->stream, static_cast<const T*>(src), *out, d);
+    return check_launch();
+  };
+  TRY(c->alloc(&c->emb, (size_t)V * d * es));
+  HIPCHK(hipMemcpyAsync(c->emb, t[0], (size_t)V * d * es, hipMemcpyDeviceToDevice, c->stream));
+  c->g_attn.resize(L);
+  c->g_ffn.resize(L);
+  c->wqkv.resize(L);
+  c->wo.resize(L);
+  c->wgu.resize(L);
+  c->wd.resize(L);
+  for (int l = 0; l < L; ++l) {
+    const void* const* p = t + 1 + 9 * l;
+    TRY(gain(p[0], &c->g_attn[l]));
+    TRY(c->alloc(&c->wqkv[l], (size_t)3 * d * d * es));
+    TRY(pack<T>(c, p[1], nullptr, d, d, 1, c->wqkv[l], 0));
+    TRY(pack<T>(c, p[2], nullptr, d, d, 1, c->wqkv[l], d));
+    TRY(pack<T>(c, p[3], nullptr, d, d, 0, c->wqkv[l], 2 * d));
+    TRY(c->alloc(&c->wo[l], (size_t)d * d * es));
+    TRY(pack<T>(c, p[4], nullptr, d, d, 0, c->wo[l], 0));
+    TRY(gain(p[5], &c->g_ffn[l]));
+    TRY(c->alloc(&c->wgu[l], (size_t)2 * F * d * es));
+    TRY(pack<T>(c, p[6], p[7], 2 * F, d, 2, c->wgu[l], 0));
+    TRY(c->alloc(&c->wd[l], (size_t)d * F * es));
+    TRY(pack<T>(c, p[8], nullptr, d, F, 0, c->wd[l], 0));
+  }
+  TRY(gain(t[1 + 9 * L], &c->g_final));
+  TRY(c->alloc(&c->wlm, (size_t)V * d * es));
+  TRY(pack<T>(c, t[2 + 9 * L], nullptr, V, d, 0, c->wlm, 0));
+
+  // rotary tables: angle = pos * theta^(-2j/dh), computed in double
+  const int half = dh / 2;
+  std::vector<float> cs((size_t)c->seq_pad * half), sn((size_t)c->seq_pad * half);
+  for (int pos = 0; pos < c->seq_pad; ++pos)
+    for (int j = 0; j < half; ++j) {
+      const double ang = (double)pos * std::pow((double)m.rope_theta, -2.0 * j / dh);
+      cs[(size_t)pos * half + j] = (float)std::cos(ang);
+      sn[(size_t)pos * half + j] = (float)std::sin(ang);
+    }
+  TRY(c->alloc(&c->rope_cos, cs.size() * sizeof(float)));
+  TRY(c->alloc(&c->rope_sin, sn.size() * sizeof(float)));
+  HIPCHK(hipMemcpyAsync(c->rope_cos, cs.data(), cs.size() * sizeof(float), hipMemcpyHostToDevice, c->stream));
+  HIPCHK(hipMemcpyAsync(c->rope_sin, sn.data(), sn.size() * sizeof(float), hipMemcpyHostToDevice, c->stream));
+
+  // KV cache (zeroed: keys past the canvas are masked but must be finite)
+  c->kv_layer = (size_t)m.max_batch * m.n_heads * c->seq_pad * dh;
+  TRY(c->alloc(&c->kc, c->kv_layer * L * es));
+  TRY(c->alloc(&c->vt, c->kv_layer * L * es));
+
+  // activations
+  TRY(c->alloc(&c->x, (size_t)c->max_rows_pad * d * sizeof(float)));
+  TRY(c->alloc(&c->xin, (size_t)c->max_rows_pad * d * es));
+  TRY(c->alloc(&c->q, (size_t)c->max_rows_pad * d * es));
+  TRY(c->alloc(&c->attn_out, (size_t)c->max_rows_pad * d * es));
+  TRY(c->alloc(&c->act, (size_t)c->max_rows_pad * F * es));
+  TRY(c->alloc(&c->xh, (size_t)c->max_head_pad * d * es));
+  c->n_vtiles = V / 32;
+  TRY(c->alloc(&c->pmax, (size_t)c->n_vtiles * c->max_head * sizeof(float)));
+  TRY(c->alloc(&c->psum, (size_t)c->n_vtiles * c->max_head * sizeof(float)));
+  TRY(c->alloc(&c->parg, (size_t)c->n_vtiles * c->max_head * sizeof(int)));
+  TRY(c->alloc(&c->conf, (size_t)c->max_head * sizeof(float)));
+  TRY(c->alloc(&c->tok, (size_t)c->max_head * sizeof(int)));
+  c->gemm_ws_floats = (size_t)16 << 20;
+  TRY(c->alloc(&c->gemm_ws, c->gemm_ws_floats * sizeof(float)));
+  c->n_counters = (size_t)1 << 16;
+  TRY(c->alloc(&c->counters, c->n_counters * sizeof(unsigned)));
+  c->attn_ws_floats = (size_t)16 << 20;
+  TRY(c->alloc(&c->attn_ws, c->attn_ws_floats * sizeof(float)));
+  c->n_attn_counters = (size_t)1 << 16;
+  TRY(c->alloc(&c->attn_counters, c->n_attn_counters * sizeof(unsigned)));
+  TRY(c->alloc(&c->d_err, 4 * sizeof(int)));
+  TRY(c->alloc(&c->d_ncommit, (size_t)m.max_batch * sizeof(int)));
+  TRY(c->alloc(&c->d_done, (size_t)m.max_batch * sizeof(int)));
+  TRY(c->alloc(&c->d_step, (size_t)m.max_batch * sizeof(int)));
+  HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&c->h_pin), (2 * m.max_batch + 4) * sizeof(int), hipHostMallocDefault));
+  HIPCHK(hipStreamSynchronize(c->stream));
+  return DLLM_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char* dllm_last_error(void) { return g_err.c_str(); }
+
+dllm_status dllm_init_weights(dllm_ctx** out, const dllm_model_cfg* cfg, const void* const* tensors, void* hip_stream) {
+  g_err.clear();
+  if (!out) return fail(DLLM_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  TRY(validate_model(cfg));
+  if (!tensors) return fail(DLLM_ERR_ARG, "tensors is NULL");
+  dllm_ctx* c = new (std::nothrow) dllm_ctx();
+  if (!c) return fail(DLLM_ERR_OOM, "host allocation failed");
+  c->cfg = *cfg;
+  c->stream = static_cast<hipStream_t>(hip_stream);
+  c->bf16 = cfg->dtype == DLLM_BF16;
+  c->esz = c->bf16 ? 2 : 4;
+  c->seq_pad = round_up(cfg->max_seq, 32);
+  c->max_rows = cfg->max_batch * cfg->max_seq;
+  c->max_rows_pad = round_up(c->max_rows, 32) + 96;  // room for a 4-tile m-group tail
+  c->max_head = cfg->max_batch * kMaxBlock;
+  c->max_head_pad = round_up(c->max_head, 32) + 96;
+  dllm_status s = c->bf16 ? init_impl<bf16_t>(c, tensors) : init_impl<float>(c, tensors);
+  if (s != DLLM_OK) {
+    std::string msg = g_err;
+    delete c;
+    g_err = msg;
+    return s;
+  }
+  *out = c;
+  return DLLM_OK;
+}
+
+void dllm_destroy(dllm_ctx* ctx) {
+  if (!ctx) return;
+  (void)hipStreamSynchronize(ctx->stream);
+  delete ctx;
+}
+
+dllm_status dllm_refresh_cache(dllm_ctx* ctx, const dllm_canvas* canvas, const dllm_decode_cfg* cfg, int32_t block_idx) {
+  g_err.clear();
+  if (!ctx || !canvas || !canvas->tokens) return fail(DLLM_ERR_ARG, "ctx, canvas and canvas->tokens must be non-NULL");
+  TRY(validate_decode(ctx, cfg));
+  return ctx->bf16 ? refresh_impl<bf16_t>(ctx, canvas, cfg, block_idx) : refresh_impl<float>(ctx, canvas, cfg, block_idx);
+}
+
+dllm_status dllm_block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg* cfg, int32_t block_idx,
+                            int32_t* n_committed, int32_t* block_done, float* dbg_logits, float* dbg_conf,
+                            int32_t* dbg_tok) {
+  g_err.clear();
+  if (!ctx || !canvas || !canvas->tokens) return fail(DLLM_ERR_ARG, "ctx, canvas and canvas->tokens must be non-NULL");
+  TRY(validate_decode(ctx, cfg));
+  if ((dbg_conf == nullptr) != (dbg_tok == nullptr)) return fail(DLLM_ERR_ARG, "dbg_conf and dbg_tok must both be set or both NULL");
+  return ctx->bf16 ? step_impl<bf16_t>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok)
+                   : step_impl<float>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok);
+}
+
+dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg* cfg, dllm_stats* stats) {
+  g_err.clear();
+  if (!ctx || !canvas || !canvas->tokens) return fail(DLLM_ERR_ARG, "ctx, canvas and canvas->tokens must be non-NULL");
+  TRY(validate_decode(ctx, cfg));
+  const auto t_start = std::chrono::steady_clock::now();
+  const dllm_model_cfg& m = ctx->cfg;
+  const int seq = cfg->prompt_len + cfg->gen_len;
+  const int n = cfg->batch * seq;
+  // the prompt holds no mask and the answer region is all mask
+  HIPCHK(hipMemsetAsync(ctx->d_err, 0, 2 * sizeof(int), ctx->stream));
+  hipLaunchKernelGGL(canvas_check_kernel, dim3(cdiv(n, 256)), dim3(256), 0, ctx->stream, canvas->tokens, n, seq,
+                     cfg->prompt_len, m.mask_id, m.vocab, ctx->d_err + 1);
+  TRY(check_launch());
+  HIPCHK(hipMemsetAsync(ctx->d_step, 0, cfg->batch * sizeof(int), ctx->stream));
+  HIPCHK(hipMemcpyAsync(ctx->h_pin + 2 * m.max_batch + 1, ctx->d_err + 1, sizeof(int), hipMemcpyDeviceToHost, ctx->stream));
+  HIPCHK(hipStreamSynchronize(ctx->stream));
+  if (ctx->h_pin[2 * m.max_batch + 1])
+    return fail(DLLM_ERR_ARG, "canvas must hold prompt tokens (no mask_id, in vocab) followed by gen_len mask_id");
+
+  hipEvent_t e0, e1;
+  HIPCHK(hipEventCreate(&e0));
+  HIPCHK(hipEventCreate(&e1));
+  double ms_refresh = 0.0;
+  int64_t steps = 0, refreshes = 0, committed = 0;
+  std::vector<int> nc(cfg->batch), done(cfg->batch);
+  std::vector<int64_t> seq_steps(cfg->batch, 0);
+  auto timed_refresh = [&](int blk) -> dllm_status {
+    HIPCHK(hipEventRecord(e0, ctx->stream));
+    TRY(dllm_refresh_cache(ctx, canvas, cfg, blk));
+    HIPCHK(hipEventRecord(e1, ctx->stream));
+    HIPCHK(hipEventSynchronize(e1));
+    float ms = 0.f;
+    HIPCHK(hipEventElapsedTime(&ms, e0, e1));
+    ms_refresh += ms;
+    ++refreshes;
+    return DLLM_OK;
+  };
+  dllm_status st = DLLM_OK;
+  const int nb = cfg->gen_len / cfg->block_len;
+  const bool bc = cfg->cache == DLLM_CACHE_BLOCK_CAUSAL;
+  const bool cached = cfg->cache == DLLM_CACHE_PREFIX || cfg->cache == DLLM_CACHE_DUAL;
+  if (bc) st = timed_refresh(-1);
+  for (int j = 0; st == DLLM_OK && j < nb; ++j) {
+    if (cached) st = timed_refresh(0);
+    int in_block = 0;
+    while (st == DLLM_OK) {
+      if (cached && cfg->refresh_every > 0 && in_block > 0 && in_block % cfg->refresh_every == 0) {
+        st = timed_refresh(0);
+        if (st != DLLM_OK) break;
+      }
+      st = dllm_block_step(ctx, canvas, cfg, j, nc.data(), done.data(), nullptr, nullptr, nullptr);
+      if (st != DLLM_OK) break;
+      ++steps;
+      ++in_block;
+      bool all_done = true, stalled = false;
+      for (int b = 0; b < cfg->batch; ++b) {
+        committed += nc[b];
+        if (nc[b] > 0) ++seq_steps[b];
+        if (!done[b]) {
+          all_done = false;
+          if (nc[b] == 0) stalled = true;
+        }
+      }
+      if (all_done) break;
+      if (stalled || in_block > cfg->block_len) {
+        st = fail(DLLM_ERR_STATE, "a step committed no token while masks remained");
+        break;
+      }
+    }
+    if (st == DLLM_OK && bc) st = timed_refresh(j);
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (st != DLLM_OK) return st;
+  if (stats) {
+    stats->steps = steps;
+    stats->refreshes = refreshes;
+    stats->committed = committed;
+    int64_t mx = 0;
+    for (int64_t v : seq_steps) mx = v > mx ? v : mx;
+    stats->max_seq_steps = mx;
+    stats->ms_refresh = ms_refresh;
+    stats->ms_total = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();
+  }
+  return DLLM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,214 @@
+/*
+ * dllm.h - C ABI of the MI355X block-wise masked-diffusion decoding library.
+ *
+ * The library runs the denoising step of Fast-dLLM-style decoding for a
+ * LLaDA-like non-causal transformer on one AMD Instinct MI355X (gfx950):
+ * recompute the current block (or block + suffix, or everything), attend to
+ * cached and fresh K/V, reduce the LM head of the still-masked positions to
+ * (argmax token, max-softmax confidence), and commit positions under the
+ * threshold, factor or fixed-count rule.
+ *
+ * Sources (web pages on diffusion-LM decoding):
+ *   [RN]  "Fast-dLLM reading notes" (zhongzhuzhou.org): eq. (3) attention;
+ *         sec. 3 PrefixCache / DualCache and Algorithm 1; Algorithm 2
+ *         (threshold + top-1 fallback); sec. 6, eq. (13), Algorithm 3 (factor).
+ *   [DS]  "Diffusion LMs: decoding steps, caches and real speed"
+ *         (tianyi-zhang-02.github.io): "what one step does" (fixed count per
+ *         step, low-confidence remasking); "KV cache" section (block diffusion
+ *         with an exact cache written after each block).
+ *   [FD]  dian8dian.com article on Fast-dLLM: cache reuse inside a block with a
+ *         global refresh after the block; threshold with top-1 fallback.
+ *
+ * Conventions for every call:
+ *   - Every call returns dllm_status; DLLM_OK is 0.  On any other status
+ *     dllm_last_error() returns a message (thread-local, valid until the next
+ *     call on that thread).  No C++ exception crosses this boundary.
+ *   - Arguments are validated before any GPU work is enqueued.  A call that
+ *     fails validation changes nothing.
+ *   - "device" pointers are HIP device allocations on the context's GPU;
+ *     "host" pointers are ordinary CPU memory.  The caller owns every pointer
+ *     it passes; the context owns its packed weights, KV cache and workspaces
+ *     (sized at dllm_init_weights from max_batch / max_seq) and frees them in
+ *     dllm_destroy.
+ *   - All GPU work is enqueued on the HIP stream given to dllm_init_weights.
+ *     A context is not thread-safe: use one context per stream.
+ *   - Token ids are int32.  The canvas of a sequence is prompt_len prompt
+ *     tokens followed by gen_len answer positions, row-major [batch, seq].
+ */
+#ifndef DLLM_H
+#define DLLM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DLLM_OK = 0,
+  DLLM_ERR_ARG = 1,      /* invalid argument or configuration                 */
+  DLLM_ERR_OOM = 2,      /* device allocation failed                          */
+  DLLM_ERR_DEVICE = 3,   /* a HIP call failed                                 */
+  DLLM_ERR_STATE = 4,    /* call out of order, or a step committed nothing    */
+  DLLM_ERR_NUMERIC = 5   /* non-finite logits / confidences were produced     */
+} dllm_status;
+
+typedef enum { DLLM_F32 = 0, DLLM_BF16 = 1 } dllm_dtype;
+
+/* Which positions a denoising step recomputes ([RN] sec. 3, Algorithm 1):
+ *   NONE   every position, every step (no cache; [DS] KV-cache section);
+ *   PREFIX current block and the masked suffix; prompt and finished blocks
+ *          come from the cache (PrefixCache);
+ *   DUAL   only the current block; prefix and suffix K/V are reused
+ *          (DualCache);
+ *   BLOCK_CAUSAL  block diffusion ([DS] KV-cache section): attention is
+ *          bidirectional inside a block and to everything before it, never to
+ *          later blocks; the prompt is one bidirectional segment; finished
+ *          blocks hold exact K/V written by one pass after the block. */
+typedef enum {
+  DLLM_CACHE_NONE = 0,
+  DLLM_CACHE_PREFIX = 1,
+  DLLM_CACHE_DUAL = 2,
+  DLLM_CACHE_BLOCK_CAUSAL = 3
+} dllm_cache_mode;
+
+/* Selection rule applied to the block's still-masked positions, ordered by
+ * confidence descending then position ascending:
+ *   THRESHOLD  commit every c_i >= tau; if none, the top one ([RN] Alg. 2);
+ *   FACTOR     commit the top n for the largest n with
+ *              (n+1)(1 - c_(n)) < factor; if none, the top one ([RN] eq. 13,
+ *              Alg. 3);
+ *   TOPK       commit the top min(k, #masked) ([DS] "what one step does").
+ * Comparisons are evaluated in float32. */
+typedef enum { DLLM_RULE_THRESHOLD = 0, DLLM_RULE_FACTOR = 1, DLLM_RULE_TOPK = 2 } dllm_rule;
+
+/* Model shape.  The architecture is pre-norm RMSNorm, rotary position
+ * embedding (rotate-half pairing, absolute canvas positions), multi-head
+ * attention softmax(QK^T / sqrt(head_dim)) V ([RN] eq. 3) without masking
+ * inside the attended range, SwiGLU feed-forward, final RMSNorm, untied LM
+ * head.  Supported: dtype DLLM_BF16 or DLLM_F32; d_model = n_heads*head_dim;
+ * head_dim in {32, 64, 128}; d_model, d_ffn, vocab multiples of 32;
+ * 0 <= mask_id < vocab. */
+typedef struct {
+  int32_t n_layers, d_model, n_heads, head_dim, d_ffn, vocab, mask_id;
+  float rms_eps, rope_theta;
+  int32_t dtype;       /* dllm_dtype: storage and MFMA input type            */
+  int32_t max_batch;   /* largest batch any later call may use               */
+  int32_t max_seq;     /* largest prompt_len + gen_len any later call may use */
+} dllm_model_cfg;
+
+/* One decode problem ([RN] Algorithm 1 inputs: prompt, answer length L,
+ * block size B, selection rule).  gen_len must be a multiple of block_len;
+ * tau in (0, 1]; factor > 0; k >= 1.  refresh_every > 0 additionally
+ * refreshes the cache every refresh_every steps inside a block (PREFIX/DUAL
+ * only; [RN] sec. 11 decouples the refresh interval from the block size);
+ * 0 refreshes only at block boundaries. */
+typedef struct {
+  int32_t batch, prompt_len, gen_len, block_len;
+  int32_t cache;          /* dllm_cache_mode */
+  int32_t rule;           /* dllm_rule       */
+  float tau, factor;
+  int32_t k;
+  int32_t refresh_every;
+} dllm_decode_cfg;
+
+/* Caller-owned decode state (all device memory).
+ *   tokens       int32 [batch, prompt_len + gen_len]; prompt then mask_id;
+ *                committed answer tokens are written in place.
+ *   bias_target  int32 [batch, gen_len] or NULL; bias_alpha float [batch,
+ *                gen_len] or NULL: a planted logit bias alpha_i added to token
+ *                target_i of answer position i before the softmax (used to make
+ *                the confidence of random-weight models controllable).
+ *   commit_step  int32 [batch, gen_len] or NULL: receives, for each answer
+ *                position, the 0-based index of the step (counted per sequence
+ *                over the whole decode) that committed it. */
+typedef struct {
+  int32_t* tokens;
+  const int32_t* bias_target;
+  const float* bias_alpha;
+  int32_t* commit_step;
+} dllm_canvas;
+
+typedef struct {
+  int64_t steps;          /* denoising steps (forward passes with a commit)   */
+  int64_t refreshes;      /* full-canvas K/V refresh passes                   */
+  int64_t committed;      /* tokens committed over all sequences              */
+  int64_t max_seq_steps;  /* largest per-sequence step count                  */
+  double ms_total;        /* wall time of the call                            */
+  double ms_refresh;      /* time in refresh / prefill / commit passes        */
+} dllm_stats;
+
+typedef struct dllm_ctx dllm_ctx;
+
+/* Create a context and load the weights.
+ *   tensors: host array of 2 + 9*n_layers DEVICE pointers, in this order:
+ *     emb [vocab, d_model];
+ *     per layer l: attn_norm [d_model], wq, wk, wv, wo [d_model, d_model],
+ *                  ffn_norm [d_model], wg, wu [d_ffn, d_model],
+ *                  wd [d_model, d_ffn];
+ *     final_norm [d_model]; lm_head [vocab, d_model].
+ *   Linear maps are row-major [out, in] (y = x W^T).  Element type is float
+ *   for DLLM_F32 and bfloat16 (uint16 bit patterns) for DLLM_BF16, norm
+ *   gains included.  The weights are copied into the context's packed layout;
+ *   the caller may free its tensors when the call returns.
+ *   hip_stream: hipStream_t on which all later work runs (NULL = default).
+ * Errors: DLLM_ERR_ARG (unsupported shape, NULL pointer), DLLM_ERR_OOM,
+ *   DLLM_ERR_DEVICE.  *out is NULL on failure. */
+dllm_status dllm_init_weights(dllm_ctx** out, const dllm_model_cfg* cfg,
+                              const void* const* tensors, void* hip_stream);
+
+/* Cache pass over the canvas (writes K and V of every layer in place).
+ *   cache PREFIX / DUAL / NONE: a full bidirectional pass over all
+ *     prompt_len + gen_len positions ([RN] Algorithm 1: initialise before
+ *     the first block, refresh before each next block).  Commits nothing.
+ *     block_idx is ignored.
+ *   cache BLOCK_CAUSAL: block_idx < 0 runs the prompt pass (prompt positions
+ *     only, bidirectional among themselves); block_idx = j >= 0 runs the
+ *     commit pass of answer block j: its final tokens attend to [0, end of
+ *     block j) and their exact K/V are stored ([DS] KV-cache section).
+ * Errors: DLLM_ERR_ARG (bad cfg, batch > max_batch, seq > max_seq),
+ *   DLLM_ERR_DEVICE. */
+dllm_status dllm_refresh_cache(dllm_ctx* ctx, const dllm_canvas* canvas,
+                               const dllm_decode_cfg* cfg, int32_t block_idx);
+
+/* One denoising step on answer block block_idx (0-based) of every sequence.
+ * The positions given by the cache mode are recomputed; their fresh K/V
+ * overwrite the cached rows they replace; the block's still-masked positions
+ * get y_i = argmax (lowest id on ties; mask_id excluded) and
+ * c_i = max softmax probability; the rule selects positions; selected
+ * positions receive y_i simultaneously ([RN] Algorithm 2 step 5).  A sequence
+ * whose block holds no mask commits nothing.
+ *   n_committed, block_done: host int32 [batch] outputs (tokens committed by
+ *     this step; 1 if the block holds no mask afterwards), or NULL.
+ *   dbg_logits: device float [batch * block_len, vocab] or NULL: biased
+ *     logits of every block row (mask_id column = -inf) - a slow debug path.
+ *   dbg_conf, dbg_tok: device float / int32 [batch * block_len] or NULL:
+ *     c_i and y_i of the block's masked rows (-1 for rows already committed).
+ * Blocks the host until the 8-byte-per-sequence result is read back.
+ * Errors: DLLM_ERR_ARG, DLLM_ERR_NUMERIC (non-finite confidence; the canvas is
+ *   left unchanged), DLLM_ERR_DEVICE. */
+dllm_status dllm_block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg* cfg,
+                            int32_t block_idx, int32_t* n_committed, int32_t* block_done,
+                            float* dbg_logits, float* dbg_conf, int32_t* dbg_tok);
+
+/* Whole decode ([RN] Algorithm 1, or block diffusion for BLOCK_CAUSAL):
+ * checks that the prompt holds no mask_id and the answer region is all
+ * mask_id, then for each block: refresh (PREFIX / DUAL) and steps until the
+ * block holds no mask in any sequence (lock-step over the batch; finished
+ * sequences commit nothing).  No refresh follows the last block.
+ *   stats: host output or NULL.
+ * Errors: DLLM_ERR_ARG, DLLM_ERR_STATE (a step committed nothing while masks
+ *   remained), DLLM_ERR_NUMERIC, DLLM_ERR_DEVICE. */
+dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg* cfg,
+                        dllm_stats* stats);
+
+/* Release every device allocation of the context.  NULL is ignored. */
+void dllm_destroy(dllm_ctx* ctx);
+
+/* Message of the last non-OK status on the calling thread ("" if none). */
+const char* dllm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DLLM_H */
