@@ -19,7 +19,14 @@ CACHE = {"none": 0, "prefix": 1, "dual": 2, "block_causal": 3}
 RULE = {"threshold": 0, "factor": 1, "topk": 2}
 
 SYMBOLS = ("dllm_init_weights", "dllm_refresh_cache", "dllm_block_step", "dllm_decode",
-           "dllm_destroy", "dllm_last_error")
+           "dllm_set_timing", "dllm_get_timing", "dllm_destroy", "dllm_last_error")
+KERNEL_CLASSES = ("embed", "rmsnorm", "qkv", "attn", "oproj", "gateup", "down", "lmhead", "merge",
+                  "select")
+
+
+class KernelTime(C.Structure):
+    _fields_ = [("launches", C.c_int64), ("ms", C.c_double), ("bytes", C.c_double),
+                ("flops", C.c_double)]
 
 
 class ModelCfg(C.Structure):
@@ -73,6 +80,10 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.dllm_block_step.restype = C.c_int
     lib.dllm_decode.argtypes = [P, C.POINTER(Canvas), C.POINTER(DecodeCfg), C.POINTER(Stats)]
     lib.dllm_decode.restype = C.c_int
+    lib.dllm_set_timing.argtypes = [P, C.c_uint32]
+    lib.dllm_set_timing.restype = C.c_int
+    lib.dllm_get_timing.argtypes = [P, C.POINTER(KernelTime), C.c_int32]
+    lib.dllm_get_timing.restype = C.c_int
     lib.dllm_destroy.argtypes = [P]
     lib.dllm_destroy.restype = None
     lib.dllm_last_error.argtypes = []
@@ -109,6 +120,20 @@ def dllm_decode(ctx: int, canvas: Canvas, cfg: DecodeCfg) -> Stats:
     st = Stats()
     check(load().dllm_decode(C.c_void_p(ctx), C.byref(canvas), C.byref(cfg), C.byref(st)))
     return st
+
+
+def dllm_set_timing(ctx: int, classes) -> None:
+    mask = 0
+    for c in classes:
+        mask |= 1 << KERNEL_CLASSES.index(c)
+    check(load().dllm_set_timing(C.c_void_p(ctx), mask))
+
+
+def dllm_get_timing(ctx: int, reset: bool = True) -> dict:
+    arr = (KernelTime * len(KERNEL_CLASSES))()
+    check(load().dllm_get_timing(C.c_void_p(ctx), arr, 1 if reset else 0))
+    return {n: dict(launches=arr[i].launches, ms=arr[i].ms, bytes=arr[i].bytes, flops=arr[i].flops)
+            for i, n in enumerate(KERNEL_CLASSES)}
 
 
 def dllm_destroy(ctx: int) -> None:

@@ -33,8 +33,7 @@ struct AttnArgs {
   int N, P, blk, block_causal;
   int qblocks, splits;
   float scale_log2;
-  float* ws;
-  unsigned* counters;
+  float* ws;          // key-share partials when splits > 1
 };
 
 __device__ __forceinline__ int attn_limit(const AttnArgs& a, int pos) {
@@ -45,7 +44,7 @@ __device__ __forceinline__ int attn_limit(const AttnArgs& a, int pos) {
 
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
-  constexpr int KF = Mfma<T>::KF;
+  constexpr int KF = Mfma32<T>::KF;
   constexpr int NQF = DH / KF;   // fragments along dh
   constexpr int ND = DH / 32;    // output d-tiles
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -102,12 +101,12 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) kf[e] = __float_as_uint(reinterpret_cast<const float*>(krow)[c * KF + 2 * e + hf]);
       }
-      s = Mfma<T>::mma(kf, qf[c], s);
+      s = Mfma32<T>::mma(kf, qf[c], s);
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = kb + acc_row(r, lane);
+      const int key = kb + acc32_row(r, lane);
       s[r] = key < limit ? s[r] * a.scale_log2 : -INFINITY;
       mx = fmaxf(mx, s[r]);
     }
@@ -129,7 +128,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
 
-    // P V: the accumulator register r of S^T holds key kb + acc_row(r, lane)
+    // P V: the accumulator register r of S^T holds key kb + acc32_row(r, lane)
     if constexpr (sizeof(T) == 2) {
       Frag16 pf[2];
 #pragma unroll
@@ -146,7 +145,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
           const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 * c + 8);
           Frag16 vf;
           vf[0] = lo.x; vf[1] = lo.y; vf[2] = hi.x; vf[3] = hi.y;
-          o[i] = Mfma<T>::mma(vf, pf[c], o[i]);
+          o[i] = Mfma32<T>::mma(vf, pf[c], o[i]);
         }
       }
     } else {
@@ -159,7 +158,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
           Frag16 pf;
 #pragma unroll
           for (int e = 0; e < 4; ++e) pf[e] = __float_as_uint(s[4 * u + e]);
-          o[i] = Mfma<T>::mma(vf, pf, o[i]);
+          o[i] = Mfma32<T>::mma(vf, pf, o[i]);
         }
       }
     }
@@ -210,31 +209,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int i = 0; i < ND; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) dst[128 + (i * 16 + r) * 64 + lane] = o[i][r];
-    __threadfence();
-    unsigned tk = 0;
-    if (lane == 0) tk = atomicAdd(&a.counters[wg], 1u);
-    tk = __shfl(tk, 0);
-    if (tk != (unsigned)a.splits - 1) return;
-    if (lane == 0) atomicExch(&a.counters[wg], 0u);
-    __threadfence();
-    M = -INFINITY;
-    for (int sp = 0; sp < a.splits; ++sp)
-      M = fmaxf(M, a.ws[((size_t)sp * gridDim.x + wg) * rec + lane]);
-    const float Mz = M == -INFINITY ? 0.f : M;
-    L = 0.f;
-#pragma unroll
-    for (int i = 0; i < ND; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
-    for (int sp = 0; sp < a.splits; ++sp) {
-      const float* src = a.ws + ((size_t)sp * gridDim.x + wg) * rec;
-      const float f = exp2f(src[lane] - Mz);
-      L += src[64 + lane] * f;
-#pragma unroll
-      for (int i = 0; i < ND; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[i][r] += src[128 + (i * 16 + r) * 64 + lane] * f;
-    }
+    return;  // attn_merge_kernel combines the key shares
   }
 
   if (!valid) return;
@@ -244,7 +219,48 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   for (int i = 0; i < ND; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      out[packed_off<T>(m, h * DH + i * 32 + acc_row(r, lane), a.d)] = Mfma<T>::store_cvt(o[i][r] * inv);
+      out[packed_off<T>(m, h * DH + i * 32 + acc32_row(r, lane), a.d)] = Elem<T>::cvt(o[i][r] * inv);
+}
+
+// Combine the key shares of a split attention launch in share order (one wave
+// per (sequence, head, 32 queries)); launched after attn_kernel on the same
+// stream, so every share is complete.
+// 256 threads: thread t handles accumulator lane t%64 and the registers
+// (i, r) with (16 i + r) % 4 == t/64.
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int nwg) {
+  constexpr int ND = DH / 32;
+  constexpr int PER = ND * 16 / 4;
+  const int lane = threadIdx.x & 63, part = threadIdx.x >> 6, wg = blockIdx.x;
+  const int qb = wg % a.qblocks, bh = wg / a.qblocks;
+  const int h = bh % a.H, b = bh / a.H;
+  const int irow = qb * 32 + (lane & 31);
+  if (irow >= a.g.nr) return;
+  const int m = b * a.g.nr + irow;
+  const size_t rec = (size_t)(ND * 16 + 2) * 64;
+  const float* base = a.ws + (size_t)wg * rec;
+  const size_t sstride = (size_t)nwg * rec;
+  float M = -INFINITY;
+  for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, base[sp * sstride + lane]);
+  const float Mz = M == -INFINITY ? 0.f : M;
+  float L = 0.f;
+  float o[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) o[q] = 0.f;
+  for (int sp = 0; sp < a.splits; ++sp) {
+    const float* src = base + sp * sstride;
+    const float f = exp2f(src[lane] - Mz);
+    L += src[64 + lane] * f;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) o[q] += src[128 + (4 * q + part) * 64 + lane] * f;
+  }
+  const float inv = 1.0f / L;
+  T* out = static_cast<T*>(a.out);
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int ir = 4 * q + part, i = ir / 16, r = ir % 16;
+    out[packed_off<T>(m, h * DH + i * 32 + acc32_row(r, lane), a.d)] = Elem<T>::cvt(o[q] * inv);
+  }
 }
 
 }  // namespace dllm

@@ -40,7 +40,6 @@ dllm_status fail(dllm_status s, const std::string& msg) {
   } while (0)
 
 constexpr int kMaxBlock = 256;      // select/commit handles a block in one workgroup
-constexpr int kTargetWGs = 512;     // aim for >= 2 workgroups per CU
 
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
@@ -79,14 +78,10 @@ struct dllm_ctx {
   int* parg = nullptr;
   float* conf = nullptr;
   int* tok = nullptr;
-  float* gemm_ws = nullptr;
-  size_t gemm_ws_floats = 0;
-  unsigned* counters = nullptr;
-  size_t n_counters = 0;
+  float* ssq = nullptr;       // [d/16][max_rows] partial sums of x^2 of the residual rows
+  float* ssq_head = nullptr;  // [d/16][max_head] same for the LM-head rows
   float* attn_ws = nullptr;
   size_t attn_ws_floats = 0;
-  unsigned* attn_counters = nullptr;
-  size_t n_attn_counters = 0;
 
   int* d_err = nullptr;       // [0] numeric error, [1] canvas check
   int* d_ncommit = nullptr;   // [max_batch]
@@ -94,9 +89,46 @@ struct dllm_ctx {
   int* d_step = nullptr;
   int* h_pin = nullptr;       // pinned: ncommit[max_batch], done[max_batch], err[2]
 
+  // kernel timing (dllm_set_timing): event pairs pending until the next read
+  struct Pending { int cls; hipEvent_t a, b; double bytes, flops; };
+  uint32_t timing_mask = 0;
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> event_pool;
+  dllm_kernel_time timing[DLLM_K_COUNT] = {};
+
   ~dllm_ctx() {
+    for (auto& p : pending) { (void)hipEventDestroy(p.a); (void)hipEventDestroy(p.b); }
+    for (auto e : event_pool) (void)hipEventDestroy(e);
     for (void* p : allocs) (void)hipFree(p);
     if (h_pin) (void)hipHostFree(h_pin);
+  }
+
+  hipEvent_t get_event() {
+    if (!event_pool.empty()) {
+      hipEvent_t e = event_pool.back();
+      event_pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+
+  // fold finished event pairs into the counters (the stream must be idle)
+  dllm_status resolve_timing() {
+    for (auto& p : pending) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, p.a, p.b) != hipSuccess) return fail(DLLM_ERR_DEVICE, "hipEventElapsedTime failed");
+      dllm_kernel_time& t = timing[p.cls];
+      t.launches += 1;
+      t.ms += ms;
+      t.bytes += p.bytes;
+      t.flops += p.flops;
+      event_pool.push_back(p.a);
+      event_pool.push_back(p.b);
+    }
+    pending.clear();
+    return DLLM_OK;
   }
 
   template <typename P>
@@ -121,6 +153,33 @@ dllm_status check_launch() {
   if (e != hipSuccess) return fail(DLLM_ERR_DEVICE, std::string("kernel launch: ") + hipGetErrorString(e));
   return DLLM_OK;
 }
+
+// Events around one launch when its class is being timed.
+struct Timed {
+  dllm_ctx* c;
+  int cls;
+  double bytes, flops;
+  hipEvent_t a = nullptr;
+  Timed(dllm_ctx* c_, int cls_, double by, double fl) : c(c_), cls(cls_), bytes(by), flops(fl) {
+    if ((c->timing_mask >> cls) & 1u) {
+      a = c->get_event();
+      if (a) (void)hipEventRecord(a, c->stream);
+    }
+  }
+  dllm_status done() {
+    TRY(check_launch());
+    if (!a) return DLLM_OK;
+    hipEvent_t b = c->get_event();
+    if (!b) return fail(DLLM_ERR_DEVICE, "hipEventCreate failed");
+    HIPCHK(hipEventRecord(b, c->stream));
+    c->pending.push_back({cls, a, b, bytes, flops});
+    if (c->pending.size() >= 4096) {
+      HIPCHK(hipStreamSynchronize(c->stream));
+      TRY(c->resolve_timing());
+    }
+    return DLLM_OK;
+  }
+};
 
 dllm_status validate_model(const dllm_model_cfg* c) {
   if (!c) return fail(DLLM_ERR_ARG, "cfg is NULL");
@@ -157,34 +216,70 @@ dllm_status validate_decode(const dllm_ctx* ctx, const dllm_decode_cfg* d) {
 // ---------------------------------------------------------------------------
 // launch helpers
 // ---------------------------------------------------------------------------
+// algorithmic bytes of the output each projection writes (see the epilogues)
+double gemm_out_bytes(int cls, int M, int N, int es) {
+  switch (cls) {
+    case DLLM_K_QKV: return (double)M * N * es;
+    case DLLM_K_GATEUP: return (double)M * (N / 2) * es;
+    case DLLM_K_LMHEAD: return 12.0 * M * (N / 16);
+    default: return 8.0 * M * N;  // residual read + write, fp32
+  }
+}
+
+// Skinny kernel for the block step (M <= 64): one workgroup per NT 16-column
+// tiles; NT = 2 when that still leaves a multiple of 256 workgroups or very
+// many of them.  Larger M goes to the LDS-tiled kernel.
+template <typename T, int MT, int NT, int U, class Epi>
+dllm_status launch_skinny(dllm_ctx* c, const GemmArgs& a, const Epi& epi) {
+  const unsigned grid = (unsigned)((a.n_tiles / NT) * a.m_groups);
+  hipLaunchKernelGGL((gemm_skinny_kernel<T, MT, NT, 8, Epi, U>), dim3(grid), dim3(512), 0, c->stream, a, epi);
+  return DLLM_OK;
+}
+
+// n-tiles per workgroup: the largest NT whose grid is either one partial
+// round (192..256 workgroups) or whole rounds of 256 (measured on MI355X for
+// the LLaDA-8B shapes); very wide outputs take NT = 2.
 template <typename T, int MT, class Epi>
-dllm_status launch_gemm_mt(dllm_ctx* c, const void* X, const void* W, int M, int N, int K, const Epi& epi) {
+dllm_status launch_skinny_nt(dllm_ctx* c, const GemmArgs& a, const Epi& epi) {
+  auto fits = [&](int nt) {
+    if (a.n_tiles % nt) return false;
+    const int g = a.n_tiles / nt;
+    return (g >= 192 && g <= 256) || g % 256 == 0;
+  };
+  if (fits(4)) return launch_skinny<T, MT, 4, (MT <= 2 ? 8 : 4)>(c, a, epi);
+  if (fits(2) || (a.n_tiles % 2 == 0 && a.n_tiles / 2 >= 2048)) return launch_skinny<T, MT, 2, 4>(c, a, epi);
+  return launch_skinny<T, MT, 1, 4>(c, a, epi);
+}
+
+// ssq (optional): partial sums of squares [K/16][ssq_ld] of the input rows;
+// X then holds x * gain and the kernel applies the per-row 1/rms.
+template <typename T, class Epi>
+dllm_status launch_gemm(dllm_ctx* c, int cls, const void* X, const void* W, int M, int N, int K, const Epi& epi,
+                        const float* ssq = nullptr, int ssq_ld = 0) {
   GemmArgs a{};
   a.X = static_cast<const Frag16*>(X);
   a.W = static_cast<const Frag16*>(W);
-  a.KT = K / Mfma<T>::KF;
-  a.n_tiles = N / 32;
-  a.m_tiles = cdiv(M, 32);
-  a.m_groups = cdiv(a.m_tiles, MT);
-  const long base = (long)a.n_tiles * a.m_groups;
-  int splits = 1;
-  // split K until the grid fills the chip; keep >= 8 fragments per wave
-  while (base * splits < kTargetWGs && a.KT / (splits * 2 * 4) >= 8) splits *= 2;
-  while (splits > 1 && ((size_t)splits * base * MT * 1024 > c->gemm_ws_floats || (size_t)base > c->n_counters))
-    splits /= 2;
-  a.splits = splits;
-  a.ws = c->gemm_ws;
-  a.counters = c->counters;
-  hipLaunchKernelGGL((gemm_stream_kernel<T, MT, Epi>), dim3((unsigned)(base * splits)), dim3(256), 0, c->stream, a, epi);
-  return check_launch();
-}
-
-template <typename T, class Epi>
-dllm_status launch_gemm(dllm_ctx* c, const void* X, const void* W, int M, int N, int K, const Epi& epi) {
-  const int mt = cdiv(M, 32);
-  if (mt <= 1) return launch_gemm_mt<T, 1>(c, X, W, M, N, K, epi);
-  if (mt <= 2) return launch_gemm_mt<T, 2>(c, X, W, M, N, K, epi);
-  return launch_gemm_mt<T, 4>(c, X, W, M, N, K, epi);
+  a.KT = K / Mfma16<T>::KF;
+  a.n_tiles = N / 16;
+  a.m_tiles = cdiv(M, 16);
+  a.ssq = ssq;
+  a.ssq_tiles = K / 16;
+  a.ssq_ld = ssq_ld;
+  a.inv_k = 1.0f / (float)K;
+  a.eps = c->cfg.rms_eps;
+  const double es = sizeof(T);
+  Timed tm(c, cls, es * ((double)N * K + (double)M * K) + gemm_out_bytes(cls, M, N, (int)es), 2.0 * M * N * K);
+  if (a.m_tiles <= 4) {
+    a.m_groups = 1;
+    if (a.m_tiles == 1) TRY((launch_skinny_nt<T, 1>(c, a, epi)));
+    else if (a.m_tiles == 2) TRY((launch_skinny_nt<T, 2>(c, a, epi)));
+    else TRY((launch_skinny_nt<T, 4>(c, a, epi)));
+  } else {
+    const int n_wg = cdiv(a.n_tiles, 8), m_wg = cdiv(a.m_tiles, 8);
+    a.m_groups = m_wg;
+    hipLaunchKernelGGL((gemm_tiled_kernel<T, Epi>), dim3((unsigned)(n_wg * m_wg)), dim3(256), 0, c->stream, a, epi);
+  }
+  return tm.done();
 }
 
 struct Fwd {
@@ -193,6 +288,8 @@ struct Fwd {
   int batch, nr, row_start;
   int N, P, blk, block_causal;
   bool kv_only;         // last layer: K/V only (cache passes)
+  int head_blk;         // > 0: rows [head_off, head_off + head_blk) of each
+  int head_off;         //      sequence feed the LM head
 };
 
 template <typename T, int DH>
@@ -215,16 +312,26 @@ dllm_status launch_attn(dllm_ctx* c, int layer, const Fwd& f) {
   const int nwg = f.batch * m.n_heads * a.qblocks;
   const int ntile = cdiv(f.N, 32);
   int splits = 1;
-  while (nwg * splits < kTargetWGs && ntile / (splits * 2) >= 8) splits *= 2;
+  while (nwg * splits < 256 && ntile / (splits * 2) >= 3) splits *= 2;
   const size_t rec = (size_t)(DH / 32 * 16 + 2) * 64;
-  while (splits > 1 && ((size_t)splits * nwg * rec > c->attn_ws_floats || (size_t)nwg > c->n_attn_counters))
-    splits /= 2;
+  while (splits > 1 && (size_t)splits * nwg * rec > c->attn_ws_floats) splits /= 2;
   a.splits = splits;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)DH));
   a.ws = c->attn_ws;
-  a.counters = c->attn_counters;
+  // algorithmic: K and V of the keys each 32-query block attends read once, Q read, O written
+  double kv = 0.0, fl = 0.0;
+  for (int qb = 0; qb < a.qblocks; ++qb) {
+    const int last = std::min(f.nr, qb * 32 + 32) - 1, nq = last - qb * 32 + 1;
+    const int pos = f.row_start + last;
+    const int kmax = !f.block_causal ? f.N : (pos < f.P ? f.P : f.P + ((pos - f.P) / f.blk + 1) * f.blk);
+    kv += 2.0 * kmax * DH * sizeof(T);
+    fl += 4.0 * nq * kmax * DH;
+  }
+  const double M = (double)f.batch * f.nr;
+  Timed tm(c, DLLM_K_ATTN, f.batch * m.n_heads * kv + 2.0 * M * m.d_model * sizeof(T), f.batch * m.n_heads * fl);
   hipLaunchKernelGGL((attn_kernel<T, DH>), dim3(nwg, splits), dim3(256), 0, c->stream, a);
-  return check_launch();
+  if (splits > 1) hipLaunchKernelGGL((attn_merge_kernel<T, DH>), dim3(nwg), dim3(256), 0, c->stream, a, nwg);
+  return tm.done();
 }
 
 template <typename T>
@@ -236,34 +343,38 @@ dllm_status attention(dllm_ctx* c, int layer, const Fwd& f) {
   }
 }
 
-template <typename T>
-dllm_status rmsnorm(dllm_ctx* c, int rows, int blk, int src_nr, int src_off, const float* gain, void* out) {
-  hipLaunchKernelGGL((rmsnorm_pack_kernel<T>), dim3(rows), dim3(256), 0, c->stream, c->x, c->cfg.d_model, blk,
-                     src_nr, src_off, gain, c->cfg.rms_eps, static_cast<T*>(out));
-  return check_launch();
-}
-
 // Model forward over rows [row_start, row_start + nr) of every sequence.
 template <typename T>
 dllm_status forward(dllm_ctx* c, const Fwd& f) {
   const dllm_model_cfg& m = c->cfg;
   const int M = f.batch * f.nr, d = m.d_model, F = m.d_ffn;
   const RowGeom g{M, f.nr, f.row_start};
+  Timed te(c, DLLM_K_EMBED, (double)M * d * (sizeof(T) + 4.0), 0.0);
   hipLaunchKernelGGL((embed_kernel<T>), dim3(M), dim3(256), 0, c->stream, f.tokens, f.seq_len, g,
-                     static_cast<const T*>(c->emb), d, m.vocab, c->x);
-  TRY(check_launch());
+                     static_cast<const T*>(c->emb), d, m.vocab, c->x, c->g_attn[0], static_cast<T*>(c->xin),
+                     c->ssq);
+  TRY(te.done());
+  T* xin = static_cast<T*>(c->xin);
+  // normalised input of the next projection over all M rows
+  auto next_norm = [&](const float* gain) { return NormOut<T>{xin, c->ssq, gain, M, M, 0, M}; };
+  const NormOut<T> none{nullptr, nullptr, nullptr, 0, 1, 0, 1};
   for (int l = 0; l < m.n_layers; ++l) {
-    TRY(rmsnorm<T>(c, M, M, M, 0, c->g_attn[l], c->xin));
     EpiQKV<T> eq{g, d, m.head_dim, m.n_heads, c->seq_pad, static_cast<T*>(c->q),
                  static_cast<T*>(c->kc) + (size_t)l * c->kv_layer, static_cast<T*>(c->vt) + (size_t)l * c->kv_layer,
                  c->rope_cos, c->rope_sin};
-    TRY(launch_gemm<T>(c, c->xin, c->wqkv[l], M, 3 * d, d, eq));
+    TRY(launch_gemm<T>(c, DLLM_K_QKV, c->xin, c->wqkv[l], M, 3 * d, d, eq, c->ssq, M));
     if (f.kv_only && l == m.n_layers - 1) break;
     TRY(attention<T>(c, l, f));
-    TRY(launch_gemm<T>(c, c->attn_out, c->wo[l], M, d, d, EpiResidual{M, d, c->x}));
-    TRY(rmsnorm<T>(c, M, M, M, 0, c->g_ffn[l], c->xin));
-    TRY(launch_gemm<T>(c, c->xin, c->wgu[l], M, 2 * F, d, EpiSwiGLU<T>{M, F, static_cast<T*>(c->act)}));
-    TRY(launch_gemm<T>(c, c->act, c->wd[l], M, d, F, EpiResidual{M, d, c->x}));
+    TRY(launch_gemm<T>(c, DLLM_K_OPROJ, c->attn_out, c->wo[l], M, d, d,
+                       EpiResidual<T>{M, d, c->x, next_norm(c->g_ffn[l]), none}));
+    TRY(launch_gemm<T>(c, DLLM_K_GATEUP, c->xin, c->wgu[l], M, 2 * F, d,
+                       EpiSwiGLU<T>{M, F, static_cast<T*>(c->act)}, c->ssq, M));
+    const bool last = l == m.n_layers - 1;
+    const NormOut<T> head = (last && f.head_blk > 0)
+        ? NormOut<T>{static_cast<T*>(c->xh), c->ssq_head, c->g_final, f.batch * f.head_blk, f.nr, f.head_off, f.head_blk}
+        : none;
+    TRY(launch_gemm<T>(c, DLLM_K_DOWN, c->act, c->wd[l], M, d, F,
+                       EpiResidual<T>{M, d, c->x, last ? none : next_norm(c->g_attn[l + 1]), head}));
   }
   return DLLM_OK;
 }
@@ -279,6 +390,8 @@ Fwd make_fwd(const dllm_ctx* c, const dllm_canvas* cv, const dllm_decode_cfg* d)
   f.blk = d->block_len;
   f.block_causal = d->cache == DLLM_CACHE_BLOCK_CAUSAL;
   f.kv_only = false;
+  f.head_blk = 0;
+  f.head_off = 0;
   return f;
 }
 
@@ -307,6 +420,8 @@ dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, in
                       int* block_done, float* dbg_logits, float* dbg_conf, int* dbg_tok) {
   const dllm_model_cfg& m = c->cfg;
   if (j < 0 || j >= d->gen_len / d->block_len) return fail(DLLM_ERR_ARG, "block_idx out of range");
+  if ((cv->bias_target == nullptr) != (cv->bias_alpha == nullptr))
+    return fail(DLLM_ERR_ARG, "bias_target and bias_alpha must both be set or both NULL");
   Fwd f = make_fwd(c, cv, d);
   const int s = d->prompt_len + j * d->block_len;
   switch (d->cache) {
@@ -314,19 +429,22 @@ dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, in
     case DLLM_CACHE_PREFIX: f.row_start = s; f.nr = f.seq_len - s; break;
     default: f.row_start = s; f.nr = d->block_len; break;
   }
-  TRY(forward<T>(c, f));
   const int B = d->block_len, HR = d->batch * B;
-  // final norm of the block rows, then LM head -> (max, sum, argmax) partials
-  TRY(rmsnorm<T>(c, HR, B, f.nr, s - f.row_start, c->g_final, c->xh));
+  // the last layer's down projection emits the final-norm input of the block rows
+  f.head_blk = B;
+  f.head_off = s - f.row_start;
+  TRY(forward<T>(c, f));
   EpiLMHead eh{HR, B, d->gen_len, s - d->prompt_len, cv->bias_target, cv->bias_alpha, m.mask_id, m.vocab,
                c->pmax, c->psum, c->parg, dbg_logits};
-  if ((cv->bias_target == nullptr) != (cv->bias_alpha == nullptr)) return fail(DLLM_ERR_ARG, "bias_target and bias_alpha must both be set or both NULL");
   hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, c->stream, c->d_err, 2, 0);
   TRY(check_launch());
-  TRY(launch_gemm<T>(c, c->xh, c->wlm, HR, m.vocab, m.d_model, eh));
-  hipLaunchKernelGGL(lm_merge_kernel, dim3(HR), dim3(256), 0, c->stream, c->pmax, c->psum, c->parg, c->n_vtiles, HR,
-                     c->conf, c->tok, c->d_err);
-  TRY(check_launch());
+  TRY(launch_gemm<T>(c, DLLM_K_LMHEAD, c->xh, c->wlm, HR, m.vocab, m.d_model, eh, c->ssq_head, HR));
+  {
+    Timed tm(c, DLLM_K_MERGE, 12.0 * c->n_vtiles * HR + 8.0 * HR, 3.0 * c->n_vtiles * HR);
+    hipLaunchKernelGGL(lm_merge_kernel, dim3(HR), dim3(256), 0, c->stream, c->pmax, c->psum, c->parg, c->n_vtiles,
+                       HR, c->conf, c->tok, c->d_err);
+    TRY(tm.done());
+  }
   SelectArgs sa{};
   sa.tokens = cv->tokens;
   sa.seq_len = f.seq_len;
@@ -348,8 +466,11 @@ dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, in
   sa.err = c->d_err;
   sa.dbg_conf = dbg_conf;
   sa.dbg_tok = dbg_tok;
-  hipLaunchKernelGGL(select_commit_kernel, dim3(d->batch), dim3(256), 0, c->stream, sa);
-  TRY(check_launch());
+  {
+    Timed tm(c, DLLM_K_SELECT, 20.0 * HR, (double)HR * B);
+    hipLaunchKernelGGL(select_commit_kernel, dim3(d->batch), dim3(256), 0, c->stream, sa);
+    TRY(tm.done());
+  }
   const int mb = c->cfg.max_batch;
   HIPCHK(hipMemcpyAsync(c->h_pin, c->d_ncommit, d->batch * sizeof(int), hipMemcpyDeviceToHost, c->stream));
   HIPCHK(hipMemcpyAsync(c->h_pin + mb, c->d_done, d->batch * sizeof(int), hipMemcpyDeviceToHost, c->stream));
@@ -437,20 +558,16 @@ dllm_status init_impl(dllm_ctx* c, const void* const* t) {
   TRY(c->alloc(&c->attn_out, (size_t)c->max_rows_pad * d * es));
   TRY(c->alloc(&c->act, (size_t)c->max_rows_pad * F * es));
   TRY(c->alloc(&c->xh, (size_t)c->max_head_pad * d * es));
-  c->n_vtiles = V / 32;
+  TRY(c->alloc(&c->ssq, (size_t)(d / 16) * c->max_rows * sizeof(float)));
+  TRY(c->alloc(&c->ssq_head, (size_t)(d / 16) * c->max_head * sizeof(float)));
+  c->n_vtiles = V / 16;
   TRY(c->alloc(&c->pmax, (size_t)c->n_vtiles * c->max_head * sizeof(float)));
   TRY(c->alloc(&c->psum, (size_t)c->n_vtiles * c->max_head * sizeof(float)));
   TRY(c->alloc(&c->parg, (size_t)c->n_vtiles * c->max_head * sizeof(int)));
   TRY(c->alloc(&c->conf, (size_t)c->max_head * sizeof(float)));
   TRY(c->alloc(&c->tok, (size_t)c->max_head * sizeof(int)));
-  c->gemm_ws_floats = (size_t)16 << 20;
-  TRY(c->alloc(&c->gemm_ws, c->gemm_ws_floats * sizeof(float)));
-  c->n_counters = (size_t)1 << 16;
-  TRY(c->alloc(&c->counters, c->n_counters * sizeof(unsigned)));
   c->attn_ws_floats = (size_t)16 << 20;
   TRY(c->alloc(&c->attn_ws, c->attn_ws_floats * sizeof(float)));
-  c->n_attn_counters = (size_t)1 << 16;
-  TRY(c->alloc(&c->attn_counters, c->n_attn_counters * sizeof(unsigned)));
   TRY(c->alloc(&c->d_err, 4 * sizeof(int)));
   TRY(c->alloc(&c->d_ncommit, (size_t)m.max_batch * sizeof(int)));
   TRY(c->alloc(&c->d_done, (size_t)m.max_batch * sizeof(int)));
@@ -483,9 +600,9 @@ dllm_status dllm_init_weights(dllm_ctx** out, const dllm_model_cfg* cfg, const v
   c->esz = c->bf16 ? 2 : 4;
   c->seq_pad = round_up(cfg->max_seq, 32);
   c->max_rows = cfg->max_batch * cfg->max_seq;
-  c->max_rows_pad = round_up(c->max_rows, 32) + 96;  // room for a 4-tile m-group tail
+  c->max_rows_pad = round_up(c->max_rows, 128);
   c->max_head = cfg->max_batch * kMaxBlock;
-  c->max_head_pad = round_up(c->max_head, 32) + 96;
+  c->max_head_pad = round_up(c->max_head, 128);
   dllm_status s = c->bf16 ? init_impl<bf16_t>(c, tensors) : init_impl<float>(c, tensors);
   if (s != DLLM_OK) {
     std::string msg = g_err;
@@ -494,6 +611,24 @@ dllm_status dllm_init_weights(dllm_ctx** out, const dllm_model_cfg* cfg, const v
     return s;
   }
   *out = c;
+  return DLLM_OK;
+}
+
+dllm_status dllm_set_timing(dllm_ctx* ctx, uint32_t class_mask) {
+  g_err.clear();
+  if (!ctx) return fail(DLLM_ERR_ARG, "ctx is NULL");
+  ctx->timing_mask = class_mask & ((1u << DLLM_K_COUNT) - 1u);
+  return DLLM_OK;
+}
+
+dllm_status dllm_get_timing(dllm_ctx* ctx, dllm_kernel_time* out, int32_t reset) {
+  g_err.clear();
+  if (!ctx || !out) return fail(DLLM_ERR_ARG, "ctx and out must be non-NULL");
+  HIPCHK(hipStreamSynchronize(ctx->stream));
+  TRY(ctx->resolve_timing());
+  for (int i = 0; i < DLLM_K_COUNT; ++i) out[i] = ctx->timing[i];
+  if (reset)
+    for (int i = 0; i < DLLM_K_COUNT; ++i) ctx->timing[i] = dllm_kernel_time{};
   return DLLM_OK;
 }
 

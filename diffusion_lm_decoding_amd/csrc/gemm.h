@@ -1,12 +1,16 @@
-// Projection GEMM  Y[m][n] = sum_k X[m][k] W[n][k]  on MFMA, with fused
-// epilogues.  X and W are packed (mfma.h).  One workgroup (4 waves) owns one
-// 32-column n-tile, MT 32-row m-tiles and one slice of K; its 4 waves split
-// the slice four ways and stream their weight fragments straight from HBM
-// (each weight byte is read once per m-group), adding into MT 32x32 fp32
-// accumulators.  Partial sums are combined in a fixed order: waves through
-// LDS, K-slices through a workspace that the last-arriving workgroup of the
-// tile reads back in slice order (a ticket counter decides who is last; the
-// order of arrival never changes the result).
+// Projection GEMM  Y[m][n] = sum_k X[m][k] W[n][k]  on 16x16 MFMA with fused
+// epilogues; X and W are packed (mfma.h).  No workgroup ever waits for or
+// reads another's partial sums, so results are bitwise reproducible and no
+// device-scope fence is needed.
+//
+//  * gemm_skinny_kernel (M <= 64, the block step): a workgroup of NW waves owns
+//    NT 16-column n-tiles and every row; its waves split K, stream their
+//    weight fragments straight from HBM once, reuse the activation fragments
+//    across the NT tiles, and add their partial accumulators through LDS in
+//    wave order.  16-wide tiles give N/16 workgroups (256 for N = 4096).
+//  * gemm_tiled_kernel (large M: cache passes, big batches): 4 waves own a
+//    128x128 output tile; fragments of both operands are staged through a
+//    double-buffered LDS ring and shared by the waves.
 #pragma once
 #include "mfma.h"
 
@@ -19,7 +23,8 @@ struct RowGeom {
 };
 
 // ---------------------------------------------------------------------------
-// epilogues: called once per (n-tile, m-tile) with the finished accumulator
+// epilogues: called once per (16-col n-tile, 16-row m-tile); lane l holds
+// rows n = 16*nt + 4*(l/16) + r (r = 0..3) of token m = 16*mt + l%16.
 // ---------------------------------------------------------------------------
 
 // Q/K/V projection: rotary embedding on q and k (the packed weight rows of
@@ -29,60 +34,98 @@ template <typename T>
 struct EpiQKV {
   RowGeom g;
   int d, dh, H, seq_pad;
-  T* q;             // [rows][d], per-head permuted dims
-  T* kc;            // [batch][H][seq_pad][dh], permuted dims
-  T* vt;            // [batch][H][dh][seq_pad], natural dims
+  T* q;             // [rows][d], per-head rotary pair order
+  T* kc;            // [batch][H][seq_pad][dh], rotary pair order
+  T* vt;            // [batch][H][dh][seq_pad], natural order
   const float* cs;  // [seq][dh/2] cos
   const float* sn;  // [seq][dh/2] sin
-  __device__ void operator()(int nt, int mt, const f32x16& acc, int lane) const {
-    const int m = mt * 32 + (lane & 31);
+  __device__ void operator()(int nt, int mt, const f32x4& acc, int lane) const {
+    const int m = mt * 16 + (lane & 15);
     if (m >= g.M) return;
     const int b = m / g.nr;
     const int pos = g.row_start + m % g.nr;
+    const int n0 = nt * 16 + 4 * (lane >> 4);
+    float v[4] = {acc[0], acc[1], acc[2], acc[3]};
+    const int region = n0 / d, nn = n0 % d, h = nn / dh, p = nn % dh;
+    if (region < 2) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int n0 = nt * 32 + 8 * q4 + 4 * (lane >> 5);
-      float v[4] = {acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
-      const int region = n0 / d, nn = n0 % d, h = nn / dh, p = nn % dh;
-      if (region < 2) {
-#pragma unroll
-        for (int t = 0; t < 4; t += 2) {
-          const int j = (p + t) >> 1;
-          const float c = cs[pos * (dh / 2) + j], s = sn[pos * (dh / 2) + j];
-          const float e = v[t], o = v[t + 1];
-          v[t] = e * c - o * s;
-          v[t + 1] = o * c + e * s;
-        }
-        T* dst = region == 0 ? q + (size_t)m * d + nn
-                             : kc + (((size_t)b * H + h) * seq_pad + pos) * dh + p;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) dst[t] = Mfma<T>::store_cvt(v[t]);
-      } else {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          vt[(((size_t)b * H + h) * dh + p + t) * seq_pad + pos] = Mfma<T>::store_cvt(v[t]);
+      for (int t = 0; t < 4; t += 2) {
+        const int j = (p + t) >> 1;
+        const float c = cs[pos * (dh / 2) + j], s = sn[pos * (dh / 2) + j];
+        const float e = v[t], o = v[t + 1];
+        v[t] = e * c - o * s;
+        v[t + 1] = o * c + e * s;
       }
+      T* dst = region == 0 ? q + (size_t)m * d + nn : kc + (((size_t)b * H + h) * seq_pad + pos) * dh + p;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) dst[t] = Elem<T>::cvt(v[t]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) vt[(((size_t)b * H + h) * dh + p + t) * seq_pad + pos] = Elem<T>::cvt(v[t]);
     }
   }
 };
 
-// Residual update x[m][n] += y (fp32 residual stream).
+// Output of a residual update that feeds an RMSNorm: the next projection's
+// packed input xg = x * gain (the per-row 1/rms factor is applied by the
+// consumer after its matmul, see GemmArgs::ssq), plus per (16-column tile,
+// row) partial sums of x^2 in a fixed order.  rows map the producer's rows to
+// the consumer's: row m -> (m / nr) * blk + (m % nr - off) when that lies in
+// [0, blk), else skipped.
+template <typename T>
+struct NormOut {
+  T* xg;             // packed [rows][d], or null (disabled)
+  float* ssq;        // [d/16][rows_out]
+  const float* gain;
+  int rows_out;      // leading dimension of ssq
+  int nr, off, blk;  // row map
+  __device__ void put(int nt, int m, const float v[4], int lane, int d) const {
+    const int i = m % nr - off;
+    const bool keep = xg != nullptr && i >= 0 && i < blk;
+    const int mo = (m / nr) * blk + i;
+    const int n0 = nt * 16 + 4 * (lane >> 4);
+    float s = v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    if (!keep) return;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) xg[packed_off<T>(mo, n0 + t, d)] = Elem<T>::cvt(v[t] * gain[n0 + t]);
+    if (lane < 16) ssq[(size_t)nt * rows_out + mo] = s;
+  }
+};
+
+// Residual update x[m][n] += y (fp32 residual stream), optionally emitting the
+// normalised input of the next projection (nxt) and of the LM head (head).
+template <typename T>
 struct EpiResidual {
   int M, ld;
   float* x;
-  __device__ void operator()(int nt, int mt, const f32x16& acc, int lane) const {
-    const int m = mt * 32 + (lane & 31);
-    if (m >= M) return;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int n0 = nt * 32 + 8 * q4 + 4 * (lane >> 5);
-      float4* p = reinterpret_cast<float4*>(x + (size_t)m * ld + n0);
+  NormOut<T> nxt, head;
+  __device__ void operator()(int nt, int mt, const f32x4& acc, int lane) const {
+    const int m = mt * 16 + (lane & 15);
+    const bool valid = m < M;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (valid) {
+      float4* p = reinterpret_cast<float4*>(x + (size_t)m * ld + nt * 16 + 4 * (lane >> 4));
       float4 r = *p;
-      r.x += acc[4 * q4];
-      r.y += acc[4 * q4 + 1];
-      r.z += acc[4 * q4 + 2];
-      r.w += acc[4 * q4 + 3];
+      r.x += acc[0];
+      r.y += acc[1];
+      r.z += acc[2];
+      r.w += acc[3];
       *p = r;
+      v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+    }
+    // the partial-sum shuffles involve every lane; invalid rows store nothing
+    const int mm = valid ? m : 0;
+    if (nxt.xg) {
+      NormOut<T> o = nxt;
+      if (!valid) o.xg = nullptr;
+      o.put(nt, mm, v, lane, ld);
+    }
+    if (head.xg) {
+      NormOut<T> o = head;
+      if (!valid) o.xg = nullptr;
+      o.put(nt, mm, v, lane, ld);
     }
   }
 };
@@ -94,24 +137,21 @@ template <typename T>
 struct EpiSwiGLU {
   int M, F;
   T* a;  // packed [rows][F]
-  __device__ void operator()(int nt, int mt, const f32x16& acc, int lane) const {
-    const int m = mt * 32 + (lane & 31);
+  __device__ void operator()(int nt, int mt, const f32x4& acc, int lane) const {
+    const int m = mt * 16 + (lane & 15);
     if (m >= M) return;
+    const int i0 = (nt * 16 + 4 * (lane >> 4)) >> 1;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int n0 = nt * 32 + 8 * q4 + 4 * (lane >> 5);
-#pragma unroll
-      for (int t = 0; t < 4; t += 2) {
-        const float gt = acc[4 * q4 + t], up = acc[4 * q4 + t + 1];
-        const float s = gt / (1.0f + expf(-gt));
-        a[packed_off<T>(m, (n0 + t) >> 1, F)] = Mfma<T>::store_cvt(s * up);
-      }
+    for (int t = 0; t < 2; ++t) {
+      const float gt = acc[2 * t], up = acc[2 * t + 1];
+      const float s = gt / (1.0f + expf(-gt));
+      a[packed_off<T>(m, i0 + t, F)] = Elem<T>::cvt(s * up);
     }
   }
 };
 
-// LM head: planted bias, mask_id excluded, then per (vocab tile, row) the
-// running (max, argmax, sum exp(l - max)) that the merge kernel combines.
+// LM head: planted bias, mask_id excluded, then per (16-entry vocab tile,
+// row) the (max, argmax, sum exp(l - max)) that the merge kernel combines.
 // Ties keep the lowest vocabulary index.  Logits never leave registers unless
 // a debug buffer is given.
 struct EpiLMHead {
@@ -125,8 +165,8 @@ struct EpiLMHead {
   float* psum;
   int* parg;
   float* dbg;             // [M][vocab] or null
-  __device__ void operator()(int nt, int mt, const f32x16& acc, int lane) const {
-    const int m = mt * 32 + (lane & 31);
+  __device__ void operator()(int nt, int mt, const f32x4& acc, int lane) const {
+    const int m = mt * 16 + (lane & 15);
     const bool valid = m < M;
     int tgt = -1;
     float al = 0.f;
@@ -135,12 +175,12 @@ struct EpiLMHead {
       tgt = target[bi];
       al = alpha[bi];
     }
-    float v[16];
+    float v[4];
     float mx = -INFINITY;
     int am = 0x7fffffff;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int voc = nt * 32 + acc_row(r, lane);
+    for (int r = 0; r < 4; ++r) {
+      const int voc = nt * 16 + acc16_row(r, lane);
       float x = acc[r];
       if (voc == tgt) x += al;
       if (voc == mask_id) x = -INFINITY;
@@ -148,16 +188,18 @@ struct EpiLMHead {
       if (x > mx) { mx = x; am = voc; }
       if (valid && dbg) dbg[(size_t)m * vocab + voc] = x;
     }
-    const float omx = __shfl_xor(mx, 32);
-    const int oam = __shfl_xor(am, 32);
-    if (omx > mx || (omx == mx && oam < am)) { mx = omx; am = oam; }
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const float omx = __shfl_xor(mx, o);
+      const int oam = __shfl_xor(am, o);
+      if (omx > mx || (omx == mx && oam < am)) { mx = omx; am = oam; }
+    }
     float s = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s += expf(v[r] - mx);
-    // fixed order: lower half-lane first
-    const float os = __shfl_xor(s, 32);
-    s = (lane < 32) ? s + os : os + s;
-    if (valid && lane < 32) {
+    for (int r = 0; r < 4; ++r) s += expf(v[r] - mx);
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    if (valid && lane < 16) {
       pmax[(size_t)nt * M + m] = mx;
       psum[(size_t)nt * M + m] = s;
       parg[(size_t)nt * M + m] = am;
@@ -166,59 +208,62 @@ struct EpiLMHead {
 };
 
 // ---------------------------------------------------------------------------
-// kernel
-// ---------------------------------------------------------------------------
 struct GemmArgs {
-  const Frag16* X;      // packed [m_tiles*32][K]
-  const Frag16* W;      // packed [n_tiles*32][K]
-  int KT;               // k fragments
-  int n_tiles, m_tiles;
-  int m_groups;         // ceil(m_tiles / MT)
-  int splits;
-  float* ws;            // splits * n_tiles * m_groups * MT * 1024 floats
-  unsigned* counters;   // n_tiles * m_groups, zero on entry, zero on exit
+  const Frag16* X;      // packed [m_tiles*16][K]
+  const Frag16* W;      // packed [n_tiles*16][K]
+  int KT;               // K / KF
+  int n_tiles, m_tiles; // 16-row tiles
+  int m_groups;
+  // RMSNorm of the input applied after the matmul: when ssq is set, X holds
+  // x * gain and row m of the result is scaled by
+  // 1 / sqrt(sum_t ssq[t][m] / K + eps), t over ssq_tiles partial sums.
+  const float* ssq;
+  int ssq_tiles, ssq_ld;
+  float inv_k, eps;
 };
 
-// Workgroup id -> (n-tile, m-group, split) with the m-groups of one n-tile on
-// the same XCD (workgroup i runs on XCD i % 8), so their shared weight tiles
-// are fetched into one L2.
-__device__ __forceinline__ int xcd_remap(int hw, int total) {
-  const int per = total / 8, rem = total % 8, x = hw % 8, slot = hw / 8;
-  if (hw >= per * 8) return hw;          // ragged tail keeps its id
-  (void)rem;
-  return x * per + slot;
+// 1/rms of row m (lanes with equal m%16 cooperate; every lane gets the result)
+__device__ __forceinline__ float row_rstd(const GemmArgs& a, int m, int lane) {
+  float s = 0.f;
+  if (m < a.ssq_ld)
+    for (int t = lane >> 4; t < a.ssq_tiles; t += 4) s += a.ssq[(size_t)t * a.ssq_ld + m];
+  s += __shfl_xor(s, 16);
+  s += __shfl_xor(s, 32);
+  return 1.0f / sqrtf(s * a.inv_k + a.eps);
 }
 
-template <typename T, int MT, class Epi>
-__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a, Epi epi) {
-  constexpr int U = 4;  // k fragments in flight per wave per batch
+// Workgroup i runs on XCD i % 8; map consecutive logical ids to one XCD so the
+// workgroups that share weight tiles share an L2.
+__device__ __forceinline__ int xcd_remap(int hw, int total) {
+  const int per = total / 8;
+  if (hw >= per * 8) return hw;
+  return (hw % 8) * per + hw / 8;
+}
+
+template <typename T, int MT, int NT, int NW, class Epi, int U = 4>
+__global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmArgs a, Epi epi) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int total = gridDim.x;
-  const int lin = xcd_remap(blockIdx.x, total);
-  const int s = lin % a.splits;
-  const int rest = lin / a.splits;
-  const int mg = rest % a.m_groups;
-  const int nt = rest / a.m_groups;
-  const int mt0 = mg * MT;
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int mg = lin % a.m_groups, ng = lin / a.m_groups;
+  const int nt0 = ng * NT, mt0 = mg * MT;
   const int nmt = min(MT, a.m_tiles - mt0);
+  const int k0 = a.KT * wave / NW, k1 = a.KT * (wave + 1) / NW;
 
-  const int k0 = (int)((long)a.KT * s / a.splits), k1 = (int)((long)a.KT * (s + 1) / a.splits);
-  const int len = k1 - k0;
-  const int a0 = k0 + len * wave / 4, a1 = k0 + len * (wave + 1) / 4;
-
-  f32x16 acc[MT];
+  f32x4 acc[NT][MT];
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+  for (int j = 0; j < NT; ++j)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    for (int i = 0; i < MT; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const Frag16* wp = a.W + (size_t)nt * a.KT * 64 + lane;
+  const Frag16* wp = a.W + (size_t)nt0 * a.KT * 64 + lane;
   const Frag16* xp = a.X + (size_t)mt0 * a.KT * 64 + lane;
-  int kt = a0;
-  for (; kt + U <= a1; kt += U) {
-    Frag16 wf[U], xf[U][MT];
+  int kt = k0;
+  for (; kt + U <= k1; kt += U) {
+    Frag16 wf[U][NT], xf[U][MT];
 #pragma unroll
-    for (int u = 0; u < U; ++u) wf[u] = __builtin_nontemporal_load(&wp[(size_t)(kt + u) * 64]);
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) wf[u][j] = __builtin_nontemporal_load(&wp[((size_t)j * a.KT + kt + u) * 64]);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -227,71 +272,150 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a, Epi epi) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
-        if (i < nmt) acc[i] = Mfma<T>::mma(wf[u], xf[u][i], acc[i]);
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+          if (i < nmt) acc[j][i] = Mfma16<T>::mma(wf[u][j], xf[u][i], acc[j][i]);
   }
-  for (; kt < a1; ++kt) {
-    const Frag16 wf = __builtin_nontemporal_load(&wp[(size_t)kt * 64]);
+  for (; kt < k1; ++kt) {
+    Frag16 wf[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) wf[j] = __builtin_nontemporal_load(&wp[((size_t)j * a.KT + kt) * 64]);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
-      if (i < nmt) acc[i] = Mfma<T>::mma(wf, xp[((size_t)i * a.KT + kt) * 64], acc[i]);
+      if (i < nmt) {
+        const Frag16 xf = xp[((size_t)i * a.KT + kt) * 64];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[j][i] = Mfma16<T>::mma(wf[j], xf, acc[j][i]);
+      }
   }
 
-  // waves 1..3 -> LDS; wave 0 adds them in order
-  __shared__ float red[3][MT][16][64];
-  if (wave > 0) {
+  if constexpr (NW > 1) {
+    __shared__ float red[NW - 1][NT * MT * 4][64];
+    if (wave > 0) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+      for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) red[wave - 1][i][r][lane] = acc[i][r];
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[wave - 1][(j * MT + i) * 4 + r][lane] = acc[j][i][r];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    for (int w = 0; w < NW - 1; ++w)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[j][i][r] += red[w][(j * MT + i) * 4 + r][lane];
   }
-  __syncthreads();
-  if (wave == 0) {
+  if (a.ssq) {
 #pragma unroll
-    for (int w = 0; w < 3; ++w)
+    for (int i = 0; i < MT; ++i) {
+      const float rs = row_rstd(a, (mt0 + i) * 16 + (lane & 15), lane);
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] += red[w][i][r][lane];
+      for (int j = 0; j < NT; ++j) acc[j][i] *= rs;
+    }
   }
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+    for (int i = 0; i < nmt; ++i) epi(nt0 + j, mt0 + i, acc[j][i], lane);
+}
 
-  if (a.splits == 1) {
-    if (wave == 0)
-      for (int i = 0; i < nmt; ++i) epi(nt, mt0 + i, acc[i], lane);
-    return;
-  }
+// 128x128 output tile per workgroup of 4 waves (2x2, 64x64 each); BK fragments
+// of both operands per LDS stage, two stages in flight.
+template <typename T, class Epi>
+__global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a, Epi epi) {
+  constexpr int BK = 2;                    // k fragments per stage
+  constexpr int TILES = 8;                 // 16-row tiles per operand per WG
+  constexpr int FR = 2 * TILES * BK;       // fragments per stage (W then X)
+  __shared__ Frag16 lds[2][FR][64];        // 2 x 32 KiB
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n_wg = (a.n_tiles + TILES - 1) / TILES;
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int wg_n = lin % n_wg, wg_m = lin / n_wg;
+  const int nt0 = wg_n * TILES, mt0 = wg_m * TILES;
+  const int wm = wave >> 1, wn = wave & 1;  // wave's 64x64 quadrant
 
-  const size_t tile_id = (size_t)nt * a.m_groups + mg;
-  if (wave == 0) {
-    float* dst = a.ws + ((size_t)s * a.n_tiles * a.m_groups + tile_id) * MT * 1024;
+  // each thread copies FR*64/256 = 8 fragments per stage
+  auto load_stage = [&](int kt, Frag16* regs) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int q = 0; q < FR * 64 / 256; ++q) {
+      const int idx = threadIdx.x + 256 * q;       // 0 .. FR*64-1
+      const int f = idx >> 6, l = idx & 63;
+      const int isx = f >= TILES * BK;
+      const int ff = f - isx * TILES * BK;
+      const int tile = ff / BK, kk = ff % BK;
+      const int k = kt + kk;
+      Frag16 v = Frag16{0u, 0u, 0u, 0u};
+      if (!isx) {
+        if (nt0 + tile < a.n_tiles && k < a.KT)
+          v = __builtin_nontemporal_load(&a.W[(((size_t)(nt0 + tile)) * a.KT + k) * 64 + l]);
+      } else {
+        if (mt0 + tile < a.m_tiles && k < a.KT) v = a.X[(((size_t)(mt0 + tile)) * a.KT + k) * 64 + l];
+      }
+      regs[q] = v;
+    }
+  };
+  auto store_stage = [&](int buf, const Frag16* regs) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dst[(i * 16 + r) * 64 + lane] = acc[i][r];
-  }
-  __threadfence();
+    for (int q = 0; q < FR * 64 / 256; ++q) {
+      const int idx = threadIdx.x + 256 * q;
+      lds[buf][idx >> 6][idx & 63] = regs[q];
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  Frag16 regs[FR * 64 / 256];
+  load_stage(0, regs);
+  store_stage(0, regs);
   __syncthreads();
-  __shared__ int s_last;
-  if (threadIdx.x == 0) {
-    const unsigned t = atomicAdd(&a.counters[tile_id], 1u);
-    s_last = (t == (unsigned)a.splits - 1);
-    if (s_last) atomicExch(&a.counters[tile_id], 0u);
+  int buf = 0;
+  for (int kt = 0; kt < a.KT; kt += BK) {
+    const bool more = kt + BK < a.KT;
+    if (more) load_stage(kt + BK, regs);
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      Frag16 wf[4], xf[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wf[j] = lds[buf][(wn * 4 + j) * BK + kk][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xf[i] = lds[buf][TILES * BK + (wm * 4 + i) * BK + kk][lane];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[j][i] = Mfma16<T>::mma(wf[j], xf[i], acc[j][i]);
+    }
+    if (more) {
+      store_stage(buf ^ 1, regs);
+      __syncthreads();
+      buf ^= 1;
+    }
   }
-  __syncthreads();
-  if (!s_last || wave != 0) return;
-  __threadfence();
+  if (a.ssq) {
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const float rs = row_rstd(a, (mt0 + wm * 4 + i) * 16 + (lane & 15), lane);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-  for (int sp = 0; sp < a.splits; ++sp) {
-    const float* src = a.ws + ((size_t)sp * a.n_tiles * a.m_groups + tile_id) * MT * 1024;
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][r] += src[(i * 16 + r) * 64 + lane];
+      for (int j = 0; j < 4; ++j) acc[j][i] *= rs;
+    }
   }
-  for (int i = 0; i < nmt; ++i) epi(nt, mt0 + i, acc[i], lane);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int nt = nt0 + wn * 4 + j;
+    if (nt >= a.n_tiles) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int mt = mt0 + wm * 4 + i;
+      if (mt < a.m_tiles) epi(nt, mt, acc[j][i], lane);
+    }
+  }
 }
 
 }  // namespace dllm

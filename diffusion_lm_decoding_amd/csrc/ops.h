@@ -27,34 +27,30 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
 }
 
 // ---- embedding: x[m] = E[token at (sequence, position) of row m] ----------
-// Token ids outside [0, vocab) are clamped (the table is never over-read).
+// x[m] = E[token of row m] (fp32 residual stream), plus the first layer's
+// normalised-input pieces: packed x * gain and per-16-column sums of x^2
+// (ssq [d/16][M]).  Token ids outside [0, vocab) are clamped (the table is
+// never over-read).
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const int* tokens, int seq_len, RowGeom g,
-                                                    const T* emb, int d, int vocab, float* x) {
+                                                    const T* emb, int d, int vocab, float* x,
+                                                    const float* gain, T* xg, float* ssq) {
   const int m = blockIdx.x;
   const int b = m / g.nr, pos = g.row_start + m % g.nr;
   const int tok = min(max(tokens[(size_t)b * seq_len + pos], 0), vocab - 1);
   const T* e = emb + (size_t)tok * d;
-  for (int k = threadIdx.x; k < d; k += 256) x[(size_t)m * d + k] = Mfma<T>::load(e + k);
-}
-
-// ---- RMSNorm: out[m] = x[src(m)] / sqrt(mean(x^2) + eps) * g, packed -------
-// src(m) = (m / blk) * src_nr + src_off + m % blk selects e.g. the block rows
-// of each sequence for the LM head.
-template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_pack_kernel(const float* x, int d, int blk, int src_nr,
-                                                           int src_off, const float* gain, float eps,
-                                                           T* out) {
-  __shared__ float sh[4];
-  const int m = blockIdx.x;
-  const int src = (m / blk) * src_nr + src_off + m % blk;
-  const float* xr = x + (size_t)src * d;
-  float ss = 0.f;
-  for (int k = threadIdx.x; k < d; k += 256) ss += xr[k] * xr[k];
-  ss = block_sum<256>(ss, sh);
-  const float r = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int k = threadIdx.x; k < d; k += 256)
-    out[packed_off<T>(m, k, d)] = Mfma<T>::store_cvt(xr[k] * r * gain[k]);
+  for (int t = threadIdx.x; t < d / 16; t += 256) {
+    float s = 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int k = t * 16 + u;
+      const float v = Elem<T>::load(e + k);
+      x[(size_t)m * d + k] = v;
+      xg[packed_off<T>(m, k, d)] = Elem<T>::cvt(v * gain[k]);
+      s += v * v;
+    }
+    ssq[(size_t)t * g.M + m] = s;
+  }
 }
 
 // ---- LM-head merge: per row, combine the vocab-tile partials ---------------
@@ -213,7 +209,7 @@ __global__ __launch_bounds__(64) void fill_i32_kernel(int* p, int n, int v) {
 template <typename T>
 __global__ __launch_bounds__(256) void to_f32_kernel(const T* src, float* dst, int n) {
   const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t < n) dst[t] = Mfma<T>::load(src + t);
+  if (t < n) dst[t] = Elem<T>::load(src + t);
 }
 
 }  // namespace dllm

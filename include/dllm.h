@@ -202,6 +202,40 @@ dllm_status dllm_block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decod
 dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg* cfg,
                         dllm_stats* stats);
 
+/* Kernel timing for measurement.  Kernel classes of one forward/step: */
+typedef enum {
+  DLLM_K_EMBED = 0,   /* token embedding gather                          */
+  DLLM_K_RMSNORM,     /* RMSNorm into the packed projection input        */
+  DLLM_K_QKV,         /* Q/K/V projection + rotary + K/V cache write     */
+  DLLM_K_ATTN,        /* attention over the cache                        */
+  DLLM_K_OPROJ,       /* output projection + residual                    */
+  DLLM_K_GATEUP,      /* gate/up projection + SwiGLU                     */
+  DLLM_K_DOWN,        /* down projection + residual                      */
+  DLLM_K_LMHEAD,      /* LM head + planted bias + (max, sum, argmax)     */
+  DLLM_K_MERGE,       /* per-row merge of the LM-head partials           */
+  DLLM_K_SELECT,      /* select / commit                                 */
+  DLLM_K_COUNT
+} dllm_kernel_class;
+
+typedef struct {
+  int64_t launches;   /* timed launches                                           */
+  double ms;          /* summed device time between HIP events around each launch */
+  double bytes;       /* summed algorithmic HBM bytes: every operand read once and
+                         every output written once (weights, activations, K/V)     */
+  double flops;       /* summed algorithmic floating-point operations              */
+} dllm_kernel_time;
+
+/* Bracket every later launch of the kernel classes in class_mask (bit i =
+ * class i) with HIP events on the context's stream; 0 turns timing off.
+ * Counters accumulate until read with reset = 1.
+ * Errors: DLLM_ERR_ARG (ctx NULL). */
+dllm_status dllm_set_timing(dllm_ctx* ctx, uint32_t class_mask);
+
+/* Wait for the stream, then copy the counters of all DLLM_K_COUNT classes to
+ * out (host array of DLLM_K_COUNT entries); reset != 0 zeroes them.
+ * Errors: DLLM_ERR_ARG, DLLM_ERR_DEVICE. */
+dllm_status dllm_get_timing(dllm_ctx* ctx, dllm_kernel_time* out, int32_t reset);
+
 /* Release every device allocation of the context.  NULL is ignored. */
 void dllm_destroy(dllm_ctx* ctx);
 
