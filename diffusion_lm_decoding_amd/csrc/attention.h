@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          pf[c][e] = (uint32_t)f32_to_bf16(s[8 * c + 2 * e]) | ((uint32_t)f32_to_bf16(s[8 * c + 2 * e + 1]) << 16);
+          pf[c][e] = Elem<T>::bits(s[8 * c + 2 * e]) | (Elem<T>::bits(s[8 * c + 2 * e + 1]) << 16);
 #pragma unroll
       for (int i = 0; i < ND; ++i) {
         const T* vrow = vt + (size_t)(i * 32 + (lane & 31)) * a.seq_pad + kb + 4 * hf;

@@ -41,6 +41,14 @@ dllm_status fail(dllm_status s, const std::string& msg) {
 
 constexpr int kMaxBlock = 256;      // select/commit handles a block in one workgroup
 
+// Compute type T of a model -> element type of the caller's tensors.  bf16
+// models run with fp16 activations, KV cache and MFMA inputs (fp32
+// accumulation): bf16's 8-bit significand, rounded at every projection input
+// over 32 layers, leaves logit noise far above the parity bound, fp16's 11 bits
+// do not, and both run at the same MFMA rate.
+template <typename T> struct InType { using type = T; };
+template <> struct InType<f16_t> { using type = bf16_t; };
+
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
@@ -246,7 +254,9 @@ dllm_status launch_skinny_nt(dllm_ctx* c, const GemmArgs& a, const Epi& epi) {
     const int g = a.n_tiles / nt;
     return (g >= 192 && g <= 256) || g % 256 == 0;
   };
-  if (fits(4)) return launch_skinny<T, MT, 4, (MT <= 2 ? 8 : 4)>(c, a, epi);
+  if constexpr (MT <= 2) {
+    if (fits(4)) return launch_skinny<T, MT, 4, 8>(c, a, epi);
+  }
   if (fits(2) || (a.n_tiles % 2 == 0 && a.n_tiles / 2 >= 2048)) return launch_skinny<T, MT, 2, 4>(c, a, epi);
   return launch_skinny<T, MT, 1, 4>(c, a, epi);
 }
@@ -350,8 +360,9 @@ dllm_status forward(dllm_ctx* c, const Fwd& f) {
   const int M = f.batch * f.nr, d = m.d_model, F = m.d_ffn;
   const RowGeom g{M, f.nr, f.row_start};
   Timed te(c, DLLM_K_EMBED, (double)M * d * (sizeof(T) + 4.0), 0.0);
-  hipLaunchKernelGGL((embed_kernel<T>), dim3(M), dim3(256), 0, c->stream, f.tokens, f.seq_len, g,
-                     static_cast<const T*>(c->emb), d, m.vocab, c->x, c->g_attn[0], static_cast<T*>(c->xin),
+  using Tin = typename InType<T>::type;
+  hipLaunchKernelGGL((embed_kernel<Tin, T>), dim3(M), dim3(256), 0, c->stream, f.tokens, f.seq_len, g,
+                     static_cast<const Tin*>(c->emb), d, m.vocab, c->x, c->g_attn[0], static_cast<T*>(c->xin),
                      c->ssq);
   TRY(te.done());
   T* xin = static_cast<T*>(c->xin);
@@ -486,15 +497,17 @@ dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, in
 
 template <typename T>
 dllm_status pack(dllm_ctx* c, const void* src, const void* src2, int rows, int K, int mode, void* dst, int row0) {
+  using Tin = typename InType<T>::type;
   const size_t n = (size_t)rows * K;
-  hipLaunchKernelGGL((pack_kernel<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, c->stream,
-                     static_cast<const T*>(src), static_cast<const T*>(src2), rows, K, mode, c->cfg.head_dim,
+  hipLaunchKernelGGL((pack_kernel<Tin, T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, c->stream,
+                     static_cast<const Tin*>(src), static_cast<const Tin*>(src2), rows, K, mode, c->cfg.head_dim,
                      static_cast<T*>(dst), row0);
   return check_launch();
 }
 
 template <typename T>
 dllm_status init_impl(dllm_ctx* c, const void* const* t) {
+  using Tin = typename InType<T>::type;
   const dllm_model_cfg& m = c->cfg;
   const int d = m.d_model, F = m.d_ffn, V = m.vocab, L = m.n_layers, dh = m.head_dim;
   const size_t es = sizeof(T);
@@ -502,11 +515,12 @@ dllm_status init_impl(dllm_ctx* c, const void* const* t) {
     if (!t[i]) return fail(DLLM_ERR_ARG, "tensor pointer " + std::to_string(i) + " is NULL");
   auto gain = [&](const void* src, float** out) -> dllm_status {
     TRY(c->alloc(out, (size_t)d * sizeof(float)));
-    hipLaunchKernelGGL((to_f32_kernel<T>), dim3(cdiv(d, 256)), dim3(256), 0, c->stream, static_cast<const T*>(src), *out, d);
+    hipLaunchKernelGGL((to_f32_kernel<Tin>), dim3(cdiv(d, 256)), dim3(256), 0, c->stream, static_cast<const Tin*>(src), *out, d);
     return check_launch();
   };
-  TRY(c->alloc(&c->emb, (size_t)V * d * es));
-  HIPCHK(hipMemcpyAsync(c->emb, t[0], (size_t)V * d * es, hipMemcpyDeviceToDevice, c->stream));
+  // the embedding table stays in the input type (rows are gathered, not multiplied)
+  TRY(c->alloc(&c->emb, (size_t)V * d * sizeof(Tin)));
+  HIPCHK(hipMemcpyAsync(c->emb, t[0], (size_t)V * d * sizeof(Tin), hipMemcpyDeviceToDevice, c->stream));
   c->g_attn.resize(L);
   c->g_ffn.resize(L);
   c->wqkv.resize(L);
@@ -603,7 +617,7 @@ dllm_status dllm_init_weights(dllm_ctx** out, const dllm_model_cfg* cfg, const v
   c->max_rows_pad = round_up(c->max_rows, 128);
   c->max_head = cfg->max_batch * kMaxBlock;
   c->max_head_pad = round_up(c->max_head, 128);
-  dllm_status s = c->bf16 ? init_impl<bf16_t>(c, tensors) : init_impl<float>(c, tensors);
+  dllm_status s = c->bf16 ? init_impl<f16_t>(c, tensors) : init_impl<float>(c, tensors);
   if (s != DLLM_OK) {
     std::string msg = g_err;
     delete c;
@@ -642,7 +656,7 @@ dllm_status dllm_refresh_cache(dllm_ctx* ctx, const dllm_canvas* canvas, const d
   g_err.clear();
   if (!ctx || !canvas || !canvas->tokens) return fail(DLLM_ERR_ARG, "ctx, canvas and canvas->tokens must be non-NULL");
   TRY(validate_decode(ctx, cfg));
-  return ctx->bf16 ? refresh_impl<bf16_t>(ctx, canvas, cfg, block_idx) : refresh_impl<float>(ctx, canvas, cfg, block_idx);
+  return ctx->bf16 ? refresh_impl<f16_t>(ctx, canvas, cfg, block_idx) : refresh_impl<float>(ctx, canvas, cfg, block_idx);
 }
 
 dllm_status dllm_block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg* cfg, int32_t block_idx,
@@ -652,7 +666,7 @@ dllm_status dllm_block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decod
   if (!ctx || !canvas || !canvas->tokens) return fail(DLLM_ERR_ARG, "ctx, canvas and canvas->tokens must be non-NULL");
   TRY(validate_decode(ctx, cfg));
   if ((dbg_conf == nullptr) != (dbg_tok == nullptr)) return fail(DLLM_ERR_ARG, "dbg_conf and dbg_tok must both be set or both NULL");
-  return ctx->bf16 ? step_impl<bf16_t>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok)
+  return ctx->bf16 ? step_impl<f16_t>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok)
                    : step_impl<float>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok);
 }
 

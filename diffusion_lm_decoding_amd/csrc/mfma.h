@@ -44,10 +44,20 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return static_cast<bf16_t>(u >> 16);
 }
 
+typedef _Float16 f16_t;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// element load / round-to-nearest-even store; bits() is the 16-bit pattern
 template <typename T> struct Elem;
 template <> struct Elem<bf16_t> {
   __device__ static __forceinline__ float load(const bf16_t* p) { return bf16_to_f32(*p); }
   __device__ static __forceinline__ bf16_t cvt(float v) { return f32_to_bf16(v); }
+  __device__ static __forceinline__ uint32_t bits(float v) { return f32_to_bf16(v); }
+};
+template <> struct Elem<f16_t> {
+  __device__ static __forceinline__ float load(const f16_t* p) { return (float)*p; }
+  __device__ static __forceinline__ f16_t cvt(float v) { return (f16_t)v; }
+  __device__ static __forceinline__ uint32_t bits(float v) { return __builtin_bit_cast(uint16_t, (f16_t)v); }
 };
 template <> struct Elem<float> {
   __device__ static __forceinline__ float load(const float* p) { return *p; }
@@ -67,6 +77,19 @@ template <> struct Mfma16<bf16_t> {
     __builtin_memcpy(&av, &a, 16);
     __builtin_memcpy(&bv, &b, 16);
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma16<f16_t> {
+  static constexpr int KF = 32;
+  static constexpr int E = 8;
+  __host__ __device__ static constexpr int lane_of(int i, int k) { return i + 16 * (k >> 3); }
+  __host__ __device__ static constexpr int slot_of(int k) { return k & 7; }
+  __device__ static __forceinline__ f32x4 mma(const Frag16& a, const Frag16& b, f32x4 c) {
+    f16x8 av, bv;
+    __builtin_memcpy(&av, &a, 16);
+    __builtin_memcpy(&bv, &b, 16);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, c, 0, 0, 0);
   }
 };
 
@@ -106,6 +129,16 @@ template <> struct Mfma32<bf16_t> {
     __builtin_memcpy(&av, &a, 16);
     __builtin_memcpy(&bv, &b, 16);
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma32<f16_t> {
+  static constexpr int KF = 16;
+  __device__ static __forceinline__ f32x16 mma(const Frag16& a, const Frag16& b, f32x16 c) {
+    f16x8 av, bv;
+    __builtin_memcpy(&av, &a, 16);
+    __builtin_memcpy(&bv, &b, 16);
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, c, 0, 0, 0);
   }
 };
 

@@ -31,20 +31,20 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
 // normalised-input pieces: packed x * gain and per-16-column sums of x^2
 // (ssq [d/16][M]).  Token ids outside [0, vocab) are clamped (the table is
 // never over-read).
-template <typename T>
+template <typename Tin, typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const int* tokens, int seq_len, RowGeom g,
-                                                    const T* emb, int d, int vocab, float* x,
+                                                    const Tin* emb, int d, int vocab, float* x,
                                                     const float* gain, T* xg, float* ssq) {
   const int m = blockIdx.x;
   const int b = m / g.nr, pos = g.row_start + m % g.nr;
   const int tok = min(max(tokens[(size_t)b * seq_len + pos], 0), vocab - 1);
-  const T* e = emb + (size_t)tok * d;
+  const Tin* e = emb + (size_t)tok * d;
   for (int t = threadIdx.x; t < d / 16; t += 256) {
     float s = 0.f;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int k = t * 16 + u;
-      const float v = Elem<T>::load(e + k);
+      const float v = Elem<Tin>::load(e + k);
       x[(size_t)m * d + k] = v;
       xg[packed_off<T>(m, k, d)] = Elem<T>::cvt(v * gain[k]);
       s += v * v;
@@ -184,13 +184,15 @@ __global__ __launch_bounds__(256) void canvas_check_kernel(const int* tokens, in
 //   mode 1: rotary pair order inside heads of size dh:
 //           dst row h*dh + p <- src row h*dh + p/2 + (p%2)*(dh/2)
 //   mode 2: interleave: dst row 2i <- src row i, dst row 2i+1 <- src2 row i
-template <typename T>
-__global__ __launch_bounds__(256) void pack_kernel(const T* src, const T* src2, int rows, int K,
+// Elements are converted from the input type Tin to the compute type T
+// (bf16 -> fp16 is exact except for |w| < 2^-17, which rounds to 2^-24 steps).
+template <typename Tin, typename T>
+__global__ __launch_bounds__(256) void pack_kernel(const Tin* src, const Tin* src2, int rows, int K,
                                                    int mode, int dh, T* dst, int row0) {
   const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= (size_t)rows * K) return;
   const int r = (int)(t / K), k = (int)(t % K);
-  const T* s = src;
+  const Tin* s = src;
   int sr = r;
   if (mode == 1) {
     const int h = r / dh, p = r % dh;
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const T* src, const T* src2, 
     s = (r & 1) ? src2 : src;
     sr = r >> 1;
   }
-  dst[packed_off<T>(row0 + r, k, K)] = s[(size_t)sr * K + k];
+  dst[packed_off<T>(row0 + r, k, K)] = Elem<T>::cvt(Elem<Tin>::load(s + (size_t)sr * K + k));
 }
 
 __global__ __launch_bounds__(64) void fill_i32_kernel(int* p, int n, int v) {

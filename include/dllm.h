@@ -92,7 +92,16 @@ typedef enum { DLLM_RULE_THRESHOLD = 0, DLLM_RULE_FACTOR = 1, DLLM_RULE_TOPK = 2
 typedef struct {
   int32_t n_layers, d_model, n_heads, head_dim, d_ffn, vocab, mask_id;
   float rms_eps, rope_theta;
-  int32_t dtype;       /* dllm_dtype: storage and MFMA input type            */
+  int32_t dtype;       /* dllm_dtype of the weights.  DLLM_F32 computes in
+                          fp32 (fp32 MFMA).  DLLM_BF16 holds the weights as
+                          fp16 copies (exact for |w| >= 2^-17) and runs fp16
+                          activations, KV cache and MFMA inputs with fp32
+                          accumulation and softmax: with bf16's 8-bit
+                          significand the rounding at each projection input
+                          compounds over deep models into logit errors of
+                          order 0.1, fp16's 11 bits keep them ~8x smaller.
+                          fp16 range: residual-stream values must stay below
+                          65504 in magnitude, else DLLM_ERR_NUMERIC.          */
   int32_t max_batch;   /* largest batch any later call may use               */
   int32_t max_seq;     /* largest prompt_len + gen_len any later call may use */
 } dllm_model_cfg;

@@ -54,14 +54,14 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, key_limit: np.ndarray
     """Eq. (3) per head.  q: [Tq, H, dh]; k, v: [Tk, H, dh]; query t sees keys
     [0, key_limit[t]).  Returns [Tq, H, dh]."""
     dh = q.shape[-1]
-    s = np.einsum("qhd,khd->hqk", q, k) / np.sqrt(dh)
+    s = (q.transpose(1, 0, 2) @ k.transpose(1, 2, 0)) / np.sqrt(dh)      # [H, Tq, Tk]
     keys = np.arange(k.shape[0])
     visible = keys[None, :] < key_limit[:, None]            # [Tq, Tk]
     s = np.where(visible[None, :, :], s, -np.inf)
     s = s - s.max(axis=-1, keepdims=True)
     p = np.exp(s)
     p = p / p.sum(axis=-1, keepdims=True)
-    return np.einsum("hqk,khd->qhd", p, v)
+    return (p @ v.transpose(1, 0, 2)).transpose(1, 0, 2)                   # [Tq, H, dh]
 
 
 class KVCache:
@@ -91,6 +91,15 @@ class OracleModel:
             keep_f64 = shape.n_params < 50_000_000
         self._cache: Dict[str, np.ndarray] = {}
         self._keep = keep_f64
+
+    def materialize(self, threads: int = 16) -> None:
+        """Widen every tensor to float64 once, in parallel (large models)."""
+        from concurrent.futures import ThreadPoolExecutor
+        self._keep = True
+        names = [n for n in self.tensors if n not in self._cache]
+        with ThreadPoolExecutor(threads) as ex:
+            for n, a in zip(names, ex.map(lambda n: _as_f64(self.tensors[n]), names)):
+                self._cache[n] = a
 
     def w(self, name: str) -> np.ndarray:
         if name in self._cache:
