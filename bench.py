@@ -1,16 +1,16 @@
 """Benchmark: committed tokens/s of block-wise masked-diffusion decoding on one
-MI355X (LLaDA-8B-shaped random model, bf16, DualCache, block 32, tau 0.9).
+MI355X (LLaDA-8B-shaped random model, DualCache, block 32, tau 0.9).
 
 One timed "step" is one whole dllm_decode of the workload: every block's
-cache refresh, every denoising step (block forward, LM head reduce,
+cache refresh, every denoising step (block forward, LM-head reduce,
 select/commit) and the per-step readback.  Inputs (weights, prompt, planted
 bias) are synthetic and already resident in HBM when timing starts.
 
 Prints one JSON line.  `roofline` is computed for the kernel class with the
-largest device time, from the library's own algorithmic byte/flop counts and
-HIP-event durations of that class's launches inside the timed region.
-`cpu_baseline` times the float64 oracle on a bounded sample of the same
-workload on the host cores.
+largest device time in the denoising steps, from the library's algorithmic
+byte/flop counts and the HIP-event durations of that class's launches inside
+the timed region (events on the library's stream).  `cpu_baseline` times the
+float64 oracle on a bounded sample of the same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -24,8 +24,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-PEAKS_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
-RIDGE = {"bf16": 2500e12 / 8e12, "f32": 157.3e12 / 8e12}
+# dense MFMA peaks (TFLOP/s): fp16/bf16 inputs, fp32 inputs
+PEAKS_TFLOPS = {"f16": 2500.0, "f32": 157.3}
 
 
 def parse():
@@ -37,9 +37,8 @@ def parse():
     p.add_argument("--batch", type=int, default=0, help="override the workload batch")
     p.add_argument("--cache", default="", help="override the cache mode")
     p.add_argument("--rule", default="", help="override the rule")
-    p.add_argument("--cpu-steps", type=int, default=2, help="oracle block steps timed for cpu_baseline")
+    p.add_argument("--cpu-steps", type=int, default=2, help="oracle denoising steps timed for cpu_baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--kernels", action="store_true", help="print the per-class kernel table to stderr")
     return p.parse_args()
 
 
@@ -47,26 +46,30 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def kernel_table(title, prof):
+    tot = sum(v["ms"] for v in prof.values()) or 1.0
+    log(f"[bench] {title}: {tot:.1f} ms of timed kernels")
+    for k, v in sorted(prof.items(), key=lambda kv: -kv[1]["ms"]):
+        if v["launches"]:
+            ms = max(v["ms"], 1e-9)
+            log(f"[bench]   {k:8s} {v['launches']:6d} launches {v['ms']:9.2f} ms ({100 * v['ms'] / tot:5.1f}%) "
+                f"{1e3 * v['ms'] / v['launches']:8.1f} us/launch {v['bytes'] / ms / 1e6:8.1f} GB/s "
+                f"{v['flops'] / ms / 1e9:8.1f} TFLOP/s")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
-              f"(see the sharding notes in DESIGN.md).", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              f"(the multi-GPU sharding plan is described in DESIGN.md).", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
 
     from diffusion_lm_decoding_amd import _lib as L
     from diffusion_lm_decoding_amd.engine import Engine
     from workloads import gen_bias, gen_prompt, gen_tensor, workload
 
-    over = {}
-    if args.batch:
-        over["batch"] = args.batch
-    if args.cache:
-        over["cache"] = args.cache
-    if args.rule:
-        over["rule"] = args.rule
+    over = {k: v for k, v in (("batch", args.batch), ("cache", args.cache), ("rule", args.rule)) if v}
     w = workload(args.workload, **over)
     shape = w.model
     dev = torch.device("cuda:0")
@@ -84,57 +87,48 @@ def main():
     prompt = gen_prompt(shape, w.batch, w.prompt_len, w.prompt_seed)
     target, alpha = gen_bias(shape, w.batch, w.gen_len, w.bias_seed, w.alpha_max)
     cfg = Engine.cfg_from_workload(w)
-    canvases = [eng.canvas(prompt, target, alpha, w.gen_len) for _ in range(args.warmup + args.steps + 1)]
+    canvases = [eng.canvas(prompt, target, alpha, w.gen_len) for _ in range(args.warmup + args.steps)]
 
-    # warmup; the first warmup decode also times every kernel class
+    # warmup; the warmup decodes also time every kernel class
     L.dllm_set_timing(eng.ctx, L.KERNEL_CLASSES)
     for i in range(args.warmup):
         st = eng.decode(canvases[i], cfg)
         log(f"[bench] warmup {i}: {st.steps} steps, {st.committed} tokens, {st.ms_total:.1f} ms "
             f"(refresh {st.ms_refresh:.1f} ms)")
     prof = L.dllm_get_timing(eng.ctx, reset=True)
-    dom = max(prof, key=lambda k: prof[k]["ms"])
-    if True:  # per-class table of the first warmup decode
-        tot = sum(v["ms"] for v in prof.values()) or 1.0
-        for k, v in sorted(prof.items(), key=lambda kv: -kv[1]["ms"]):
-            if v["launches"]:
-                log(f"[bench]   {k:8s} {v['launches']:6d} launches {v['ms']:9.2f} ms ({100 * v['ms'] / tot:5.1f}%) "
-                    f"{v['bytes'] / max(v['ms'], 1e-9) / 1e6:8.1f} GB/s {v['flops'] / max(v['ms'], 1e-9) / 1e9:8.1f} TFLOP/s")
+    kernel_table("denoising-step kernels (warmup)", prof["step"])
+    kernel_table("cache-pass kernels (warmup)", prof["cache"])
+    dom = max(prof["step"], key=lambda k: prof["step"][k]["ms"])
 
     # timed region: only the dominant class is bracketed by events
     L.dllm_set_timing(eng.ctx, [dom])
     torch.cuda.synchronize(dev)
     t_start = time.perf_counter()
-    stats = []
-    for i in range(args.steps):
-        stats.append(eng.decode(canvases[args.warmup + i], cfg))
+    stats = [eng.decode(canvases[args.warmup + i], cfg) for i in range(args.steps)]
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t_start
     L.dllm_set_timing(eng.ctx, [])
-    kt = L.dllm_get_timing(eng.ctx, reset=True)[dom]
+    kt = L.dllm_get_timing(eng.ctx, reset=True)["step"][dom]
 
     committed = sum(s.committed for s in stats)
     steps = sum(s.steps for s in stats)
     refresh_ms = sum(s.ms_refresh for s in stats)
-    value = committed / elapsed
-    dtype = "bf16" if shape.dtype == "bf16" else "f32"
+    dtype = "f16" if shape.dtype == "bf16" else "f32"
+    n = max(kt["launches"], 1)
     intensity = kt["flops"] / max(kt["bytes"], 1.0)
-    per_launch_ms = kt["ms"] / max(kt["launches"], 1)
-    if intensity < RIDGE[dtype]:
+    ridge = PEAKS_TFLOPS[dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if intensity < ridge:
         roof = {"bound": "hbm", "achieved": kt["bytes"] / kt["ms"] / 1e6, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": kt["flops"] / kt["ms"] / 1e9, "peak": PEAKS_TFLOPS[dtype], "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["kernel"] = dom
-    roof["launches"] = kt["launches"]
-    roof["ms_per_launch"] = per_launch_ms
-    roof["bytes_per_launch"] = kt["bytes"] / max(kt["launches"], 1)
-    roof["flops_per_launch"] = kt["flops"] / max(kt["launches"], 1)
+        roof = {"bound": "mfma", "achieved": kt["flops"] / kt["ms"] / 1e9, "peak": PEAKS_TFLOPS[dtype],
+                "unit": "TFLOP/s"}
+    roof.update(frac=roof["achieved"] / roof["peak"], traffic=None, kernel=f"{dom} projection (denoising step)",
+                launches=kt["launches"], us_per_launch=1e3 * kt["ms"] / n,
+                bytes_per_launch=kt["bytes"] / n, flops_per_launch=kt["flops"] / n)
 
     out = {
         "metric": "committed tokens/s, LLaDA-8B-shape DualCache B=32 tau=0.9; % of HBM/MFMA peak",
-        "value": value,
+        "value": committed / elapsed,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -144,46 +138,46 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": dtype,
-        "data": "synthetic (counter-hash random weights, uniform prompt, planted logit bias)",
+        "data": "synthetic (counter-hash random weights, uniform random prompt, planted logit bias)",
         "config": {"workload": w.name, "batch": w.batch, "prompt_len": w.prompt_len, "gen_len": w.gen_len,
                    "block_len": w.block_len, "cache": w.cache, "rule": w.rule, "tau": w.tau,
-                   "alpha_max": w.alpha_max},
+                   "alpha_max": w.alpha_max, "weights": shape.dtype},
         "denoise_steps_per_s": steps / elapsed,
         "tokens_per_denoise_step": committed / max(steps, 1),
         "ms_per_denoise_step": (elapsed * 1e3 - refresh_ms) / max(steps, 1),
         "ms_refresh_per_decode": refresh_ms / args.steps,
         "roofline": roof,
     }
-
+    eng.close()
+    del eng
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, host_weights, w, prompt, target, alpha, args.cpu_steps)
-    eng.close()
     print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(shape, weights, w, prompt, target, alpha, n_steps):
-    """The float64 oracle on a bounded sample: n_steps DualCache denoising steps
-    of block 0 of sequence 0 (cache from one refresh-free initialisation: the
-    step cost does not depend on the cached values)."""
-    import numpy as np
+    """The float64 oracle on a bounded sample of the workload: n_steps
+    DualCache denoising steps of block 0 of sequence 0.  The weights are
+    widened to float64 before timing; the cache starts zeroed (a step's cost
+    does not depend on the cached values); refresh passes are not timed."""
     from threadpoolctl import threadpool_info
 
     from oracle import OracleDecoder, OracleModel
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    om = OracleModel(shape, weights, keep_f64=False)
+    om = OracleModel(shape, weights)
+    om.materialize()
     dec = OracleDecoder(om, w.prompt_len, w.gen_len, w.block_len, cache=w.cache, rule=w.rule,
                         tau=w.tau, factor=w.factor, k=w.k)
     st = dec.new_state(prompt[0], target[0], alpha[0])
     t0 = time.perf_counter()
     committed = 0
     for _ in range(n_steps):
-        rec = dec.step(st, 0)
-        committed += len(rec.selected)
+        committed += len(dec.step(st, 0).selected)
     dt = time.perf_counter() - t0
     log(f"[bench] oracle: {n_steps} steps, {committed} tokens in {dt:.1f} s on {threads} threads")
     return {"value": committed / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_steps} DualCache denoising steps (block 0, sequence 0, float64) of {w.name}; "
-                      f"refresh passes excluded", "seconds": dt}
+            "sample": f"{n_steps} DualCache denoising steps (block 0, sequence 0, float64 NumPy) of "
+                      f"{w.name}; refresh passes not included", "seconds": dt}
 
 
 if __name__ == "__main__":

@@ -130,10 +130,15 @@ def dllm_set_timing(ctx: int, classes) -> None:
 
 
 def dllm_get_timing(ctx: int, reset: bool = True) -> dict:
-    arr = (KernelTime * len(KERNEL_CLASSES))()
+    """{"step": {class: counters}, "cache": {class: counters}}"""
+    n = len(KERNEL_CLASSES)
+    arr = (KernelTime * (2 * n))()
     check(load().dllm_get_timing(C.c_void_p(ctx), arr, 1 if reset else 0))
-    return {n: dict(launches=arr[i].launches, ms=arr[i].ms, bytes=arr[i].bytes, flops=arr[i].flops)
-            for i, n in enumerate(KERNEL_CLASSES)}
+    out = {}
+    for part, off in (("step", 0), ("cache", n)):
+        out[part] = {k: dict(launches=arr[off + i].launches, ms=arr[off + i].ms, bytes=arr[off + i].bytes,
+                             flops=arr[off + i].flops) for i, k in enumerate(KERNEL_CLASSES)}
+    return out
 
 
 def dllm_destroy(ctx: int) -> None:

@@ -100,9 +100,10 @@ struct dllm_ctx {
   // kernel timing (dllm_set_timing): event pairs pending until the next read
   struct Pending { int cls; hipEvent_t a, b; double bytes, flops; };
   uint32_t timing_mask = 0;
+  int timing_slot = 0;        // 0 during denoising steps, DLLM_K_COUNT during cache passes
   std::vector<Pending> pending;
   std::vector<hipEvent_t> event_pool;
-  dllm_kernel_time timing[DLLM_K_COUNT] = {};
+  dllm_kernel_time timing[2 * DLLM_K_COUNT] = {};
 
   ~dllm_ctx() {
     for (auto& p : pending) { (void)hipEventDestroy(p.a); (void)hipEventDestroy(p.b); }
@@ -180,7 +181,7 @@ struct Timed {
     hipEvent_t b = c->get_event();
     if (!b) return fail(DLLM_ERR_DEVICE, "hipEventCreate failed");
     HIPCHK(hipEventRecord(b, c->stream));
-    c->pending.push_back({cls, a, b, bytes, flops});
+    c->pending.push_back({cls + c->timing_slot, a, b, bytes, flops});
     if (c->pending.size() >= 4096) {
       HIPCHK(hipStreamSynchronize(c->stream));
       TRY(c->resolve_timing());
@@ -255,7 +256,7 @@ dllm_status launch_skinny_nt(dllm_ctx* c, const GemmArgs& a, const Epi& epi) {
     return (g >= 192 && g <= 256) || g % 256 == 0;
   };
   if constexpr (MT <= 2) {
-    if (fits(4)) return launch_skinny<T, MT, 4, 8>(c, a, epi);
+    if (fits(4)) return launch_skinny<T, MT, 4, 4>(c, a, epi);
   }
   if (fits(2) || (a.n_tiles % 2 == 0 && a.n_tiles / 2 >= 2048)) return launch_skinny<T, MT, 2, 4>(c, a, epi);
   return launch_skinny<T, MT, 1, 4>(c, a, epi);
@@ -640,9 +641,9 @@ dllm_status dllm_get_timing(dllm_ctx* ctx, dllm_kernel_time* out, int32_t reset)
   if (!ctx || !out) return fail(DLLM_ERR_ARG, "ctx and out must be non-NULL");
   HIPCHK(hipStreamSynchronize(ctx->stream));
   TRY(ctx->resolve_timing());
-  for (int i = 0; i < DLLM_K_COUNT; ++i) out[i] = ctx->timing[i];
+  for (int i = 0; i < 2 * DLLM_K_COUNT; ++i) out[i] = ctx->timing[i];
   if (reset)
-    for (int i = 0; i < DLLM_K_COUNT; ++i) ctx->timing[i] = dllm_kernel_time{};
+    for (int i = 0; i < 2 * DLLM_K_COUNT; ++i) ctx->timing[i] = dllm_kernel_time{};
   return DLLM_OK;
 }
 
@@ -656,7 +657,11 @@ dllm_status dllm_refresh_cache(dllm_ctx* ctx, const dllm_canvas* canvas, const d
   g_err.clear();
   if (!ctx || !canvas || !canvas->tokens) return fail(DLLM_ERR_ARG, "ctx, canvas and canvas->tokens must be non-NULL");
   TRY(validate_decode(ctx, cfg));
-  return ctx->bf16 ? refresh_impl<f16_t>(ctx, canvas, cfg, block_idx) : refresh_impl<float>(ctx, canvas, cfg, block_idx);
+  ctx->timing_slot = DLLM_K_COUNT;
+  const dllm_status s = ctx->bf16 ? refresh_impl<f16_t>(ctx, canvas, cfg, block_idx)
+                                  : refresh_impl<float>(ctx, canvas, cfg, block_idx);
+  ctx->timing_slot = 0;
+  return s;
 }
 
 dllm_status dllm_block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg* cfg, int32_t block_idx,

@@ -255,6 +255,23 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmArgs a, Epi ep
 #pragma unroll
     for (int i = 0; i < MT; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // this wave's share of the input rows' sums of squares: tiles t with
+  // t % (4 NW) == 4 wave + lane/16, loaded now so the latency hides behind
+  // the weight stream, combined after the main loop
+  constexpr int QS = 8;  // covers 32*NW tiles (K <= 4096 at NW = 8) without a second pass
+  float ssv[MT][QS];
+  const int t_first = 4 * wave + (lane >> 4);
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int m = (mt0 + i) * 16 + (lane & 15);
+    const bool ok = a.ssq && i < nmt && m < a.ssq_ld;
+#pragma unroll
+    for (int q = 0; q < QS; ++q) {
+      const int t = t_first + q * 4 * NW;
+      ssv[i][q] = (ok && t < a.ssq_tiles) ? a.ssq[(size_t)t * a.ssq_ld + m] : 0.f;
+    }
+  }
+
   const Frag16* wp = a.W + (size_t)nt0 * a.KT * 64 + lane;
   const Frag16* xp = a.X + (size_t)mt0 * a.KT * 64 + lane;
   int kt = k0;
@@ -290,6 +307,26 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmArgs a, Epi ep
       }
   }
 
+  // per-wave sums of squares (tiles past the prefetched ones, for K > 4096,
+  // are read here), then the four lane groups of each row
+  float ssq_part[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < QS; ++q) s += ssv[i][q];
+    const int m = (mt0 + i) * 16 + (lane & 15);
+    if (a.ssq && i < nmt && m < a.ssq_ld)
+      for (int t = t_first + QS * 4 * NW; t < a.ssq_tiles; t += 4 * NW) s += a.ssq[(size_t)t * a.ssq_ld + m];
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    ssq_part[i] = s;
+  }
+  __shared__ float ssq_red[NW][MT][16];
+  if (a.ssq && lane < 16) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) ssq_red[wave][i][lane] = ssq_part[i];
+  }
   if constexpr (NW > 1) {
     __shared__ float red[NW - 1][NT * MT * 4][64];
     if (wave > 0) {
@@ -309,11 +346,15 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmArgs a, Epi ep
         for (int i = 0; i < MT; ++i)
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[j][i][r] += red[w][(j * MT + i) * 4 + r][lane];
+  } else {
+    __syncthreads();
   }
   if (a.ssq) {
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-      const float rs = row_rstd(a, (mt0 + i) * 16 + (lane & 15), lane);
+      float s = 0.f;
+      for (int w = 0; w < NW; ++w) s += ssq_red[w][i][lane & 15];
+      const float rs = 1.0f / sqrtf(s * a.inv_k + a.eps);
 #pragma unroll
       for (int j = 0; j < NT; ++j) acc[j][i] *= rs;
     }

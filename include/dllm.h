@@ -240,8 +240,10 @@ typedef struct {
  * Errors: DLLM_ERR_ARG (ctx NULL). */
 dllm_status dllm_set_timing(dllm_ctx* ctx, uint32_t class_mask);
 
-/* Wait for the stream, then copy the counters of all DLLM_K_COUNT classes to
- * out (host array of DLLM_K_COUNT entries); reset != 0 zeroes them.
+/* Wait for the stream, then copy the counters to out, a host array of
+ * 2 * DLLM_K_COUNT entries: [0, DLLM_K_COUNT) for launches made by
+ * dllm_block_step (denoising steps), [DLLM_K_COUNT, 2 * DLLM_K_COUNT) for
+ * launches made by dllm_refresh_cache (cache passes); reset != 0 zeroes them.
  * Errors: DLLM_ERR_ARG, DLLM_ERR_DEVICE. */
 dllm_status dllm_get_timing(dllm_ctx* ctx, dllm_kernel_time* out, int32_t reset);
 
