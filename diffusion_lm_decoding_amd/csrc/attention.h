@@ -23,6 +23,8 @@
 
 namespace dllm {
 
+constexpr int kMaxAttnSplits = 8;   // key shares per (sequence, head, 32 queries)
+
 struct AttnArgs {
   const void* q;      // T [rows][d]
   const void* kc;     // T, layer base
@@ -92,17 +94,31 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
     const T* krow = kc + (size_t)(kb + (lane & 31)) * DH;
+    // 16-bit types: the tile's K and V fragments are requested together, so the
+    // V latency hides behind the QK^T products and the softmax
+    Frag16 kf[NQF];
+    Frag16 vf[ND][2];
+    if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int c = 0; c < NQF; ++c) {
-      Frag16 kf;
-      if constexpr (sizeof(T) == 2) {
-        kf = *reinterpret_cast<const Frag16*>(krow + c * KF + 8 * hf);
-      } else {
+      for (int c = 0; c < NQF; ++c) kf[c] = *reinterpret_cast<const Frag16*>(krow + c * KF + 8 * hf);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) kf[e] = __float_as_uint(reinterpret_cast<const float*>(krow)[c * KF + 2 * e + hf]);
+      for (int i = 0; i < ND; ++i) {
+        const T* vrow = vt + (size_t)(i * 32 + (lane & 31)) * a.seq_pad + kb + 4 * hf;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 16 * c);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 * c + 8);
+          vf[i][c] = Frag16{lo.x, lo.y, hi.x, hi.y};
+        }
       }
-      s = Mfma32<T>::mma(kf, qf[c], s);
+    } else {
+#pragma unroll
+      for (int c = 0; c < NQF; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kf[c][e] = __float_as_uint(reinterpret_cast<const float*>(krow)[c * KF + 2 * e + hf]);
     }
+#pragma unroll
+    for (int c = 0; c < NQF; ++c) s = Mfma32<T>::mma(kf[c], qf[c], s);
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -137,17 +153,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         for (int e = 0; e < 4; ++e)
           pf[c][e] = Elem<T>::bits(s[8 * c + 2 * e]) | (Elem<T>::bits(s[8 * c + 2 * e + 1]) << 16);
 #pragma unroll
-      for (int i = 0; i < ND; ++i) {
-        const T* vrow = vt + (size_t)(i * 32 + (lane & 31)) * a.seq_pad + kb + 4 * hf;
+      for (int i = 0; i < ND; ++i)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 16 * c);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 * c + 8);
-          Frag16 vf;
-          vf[0] = lo.x; vf[1] = lo.y; vf[2] = hi.x; vf[3] = hi.y;
-          o[i] = Mfma32<T>::mma(vf, pf[c], o[i]);
-        }
-      }
+        for (int c = 0; c < 2; ++c) o[i] = Mfma32<T>::mma(vf[i][c], pf[c], o[i]);
     } else {
 #pragma unroll
       for (int i = 0; i < ND; ++i) {
@@ -240,19 +248,31 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int nwg) {
   const size_t rec = (size_t)(ND * 16 + 2) * 64;
   const float* base = a.ws + (size_t)wg * rec;
   const size_t sstride = (size_t)nwg * rec;
+  // every load is issued before the first use (splits <= kMaxAttnSplits)
+  float mv[kMaxAttnSplits], lv[kMaxAttnSplits], ov[kMaxAttnSplits][PER];
+#pragma unroll
+  for (int sp = 0; sp < kMaxAttnSplits; ++sp) {
+    const bool on = sp < a.splits;
+    const float* src = base + sp * sstride;
+    mv[sp] = on ? src[lane] : -INFINITY;
+    lv[sp] = on ? src[64 + lane] : 0.f;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) ov[sp][q] = on ? src[128 + (4 * q + part) * 64 + lane] : 0.f;
+  }
   float M = -INFINITY;
-  for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, base[sp * sstride + lane]);
+#pragma unroll
+  for (int sp = 0; sp < kMaxAttnSplits; ++sp) M = fmaxf(M, mv[sp]);
   const float Mz = M == -INFINITY ? 0.f : M;
   float L = 0.f;
   float o[PER];
 #pragma unroll
   for (int q = 0; q < PER; ++q) o[q] = 0.f;
-  for (int sp = 0; sp < a.splits; ++sp) {
-    const float* src = base + sp * sstride;
-    const float f = exp2f(src[lane] - Mz);
-    L += src[64 + lane] * f;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) o[q] += src[128 + (4 * q + part) * 64 + lane] * f;
+  for (int sp = 0; sp < kMaxAttnSplits; ++sp) {
+    const float f = sp < a.splits ? exp2f(mv[sp] - Mz) : 0.f;
+    L += lv[sp] * f;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) o[q] += ov[sp][q] * f;
   }
   const float inv = 1.0f / L;
   T* out = static_cast<T*>(a.out);

@@ -241,7 +241,10 @@ double gemm_out_bytes(int cls, int M, int N, int es) {
 template <typename T, int MT, int NT, int U, class Epi>
 dllm_status launch_skinny(dllm_ctx* c, const GemmArgs& a, const Epi& epi) {
   const unsigned grid = (unsigned)((a.n_tiles / NT) * a.m_groups);
-  hipLaunchKernelGGL((gemm_skinny_kernel<T, MT, NT, 8, Epi, U>), dim3(grid), dim3(512), 0, c->stream, a, epi);
+  if (grid <= 256)
+    hipLaunchKernelGGL((gemm_skinny_kernel<T, MT, NT, 8, Epi, U, true>), dim3(grid), dim3(512), 0, c->stream, a, epi);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<T, MT, NT, 8, Epi, U, false>), dim3(grid), dim3(512), 0, c->stream, a, epi);
   return DLLM_OK;
 }
 
@@ -255,10 +258,12 @@ dllm_status launch_skinny_nt(dllm_ctx* c, const GemmArgs& a, const Epi& epi) {
     const int g = a.n_tiles / nt;
     return (g >= 192 && g <= 256) || g % 256 == 0;
   };
+  // U (fragments per pipelined batch) keeps both register sets in VGPRs
   if constexpr (MT <= 2) {
-    if (fits(4)) return launch_skinny<T, MT, 4, 4>(c, a, epi);
+    if (fits(4)) return launch_skinny<T, MT, 4, 2>(c, a, epi);
   }
-  if (fits(2) || (a.n_tiles % 2 == 0 && a.n_tiles / 2 >= 2048)) return launch_skinny<T, MT, 2, 4>(c, a, epi);
+  if (fits(2) || (a.n_tiles % 2 == 0 && a.n_tiles / 2 >= 2048))
+    return launch_skinny<T, MT, 2, (MT <= 2 ? 4 : 2)>(c, a, epi);
   return launch_skinny<T, MT, 1, 4>(c, a, epi);
 }
 
@@ -323,7 +328,7 @@ dllm_status launch_attn(dllm_ctx* c, int layer, const Fwd& f) {
   const int nwg = f.batch * m.n_heads * a.qblocks;
   const int ntile = cdiv(f.N, 32);
   int splits = 1;
-  while (nwg * splits < 256 && ntile / (splits * 2) >= 3) splits *= 2;
+  while (nwg * splits < 256 && ntile / (splits * 2) >= 3 && splits < kMaxAttnSplits) splits *= 2;
   const size_t rec = (size_t)(DH / 32 * 16 + 2) * 64;
   while (splits > 1 && (size_t)splits * nwg * rec > c->attn_ws_floats) splits /= 2;
   a.splits = splits;

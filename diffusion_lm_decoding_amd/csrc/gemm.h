@@ -240,7 +240,9 @@ __device__ __forceinline__ int xcd_remap(int hw, int total) {
   return (hw % 8) * per + hw / 8;
 }
 
-template <typename T, int MT, int NT, int NW, class Epi, int U = 4>
+// PIPE: two register sets, the next batch in flight during the current MFMAs
+// (for grids of at most one workgroup per CU); otherwise one set.
+template <typename T, int MT, int NT, int NW, class Epi, int U = 4, bool PIPE = true>
 __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmArgs a, Epi epi) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -258,53 +260,96 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmArgs a, Epi ep
   // this wave's share of the input rows' sums of squares: tiles t with
   // t % (4 NW) == 4 wave + lane/16, loaded now so the latency hides behind
   // the weight stream, combined after the main loop
+  // Loads are unconditional (indices clamped into range, out-of-range values
+  // masked at use) so the loop bodies stay branch-free and the compiler can
+  // wait on individual loads instead of draining all of them before each MFMA.
   constexpr int QS = 8;  // covers 32*NW tiles (K <= 4096 at NW = 8) without a second pass
   float ssv[MT][QS];
   const int t_first = 4 * wave + (lane >> 4);
+  if (a.ssq) {
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    const int m = (mt0 + i) * 16 + (lane & 15);
-    const bool ok = a.ssq && i < nmt && m < a.ssq_ld;
+    for (int i = 0; i < MT; ++i) {
+      const int m = min((mt0 + i) * 16 + (lane & 15), a.ssq_ld - 1);
 #pragma unroll
-    for (int q = 0; q < QS; ++q) {
-      const int t = t_first + q * 4 * NW;
-      ssv[i][q] = (ok && t < a.ssq_tiles) ? a.ssq[(size_t)t * a.ssq_ld + m] : 0.f;
+      for (int q = 0; q < QS; ++q)
+        ssv[i][q] = a.ssq[(size_t)min(t_first + q * 4 * NW, a.ssq_tiles - 1) * a.ssq_ld + m];
     }
   }
 
   const Frag16* wp = a.W + (size_t)nt0 * a.KT * 64 + lane;
-  const Frag16* xp = a.X + (size_t)mt0 * a.KT * 64 + lane;
-  int kt = k0;
-  for (; kt + U <= k1; kt += U) {
-    Frag16 wf[U][NT], xf[U][MT];
+  const Frag16* xq[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) xq[i] = a.X + (size_t)min(mt0 + i, a.m_tiles - 1) * a.KT * 64 + lane;
+
+  // batches of U fragments in two register sets: batch b+1 is requested
+  // before batch b feeds the MFMAs
+  Frag16 wa[U][NT], xa[U][MT], wb[U][NT], xb[U][MT];
+  auto load = [&](Frag16 (&wf)[U][NT], Frag16 (&xf)[U][MT], int k) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int j = 0; j < NT; ++j) wf[u][j] = __builtin_nontemporal_load(&wp[((size_t)j * a.KT + kt + u) * 64]);
+      for (int j = 0; j < NT; ++j) wf[u][j] = __builtin_nontemporal_load(&wp[((size_t)j * a.KT + k + u) * 64]);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
-        if (i < nmt) xf[u][i] = xp[((size_t)i * a.KT + kt + u) * 64];
+      for (int i = 0; i < MT; ++i) xf[u][i] = xq[i][(size_t)(k + u) * 64];
+  };
+  auto compute = [&](const Frag16 (&wf)[U][NT], const Frag16 (&xf)[U][MT]) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int j = 0; j < NT; ++j)
 #pragma unroll
+        for (int i = 0; i < MT; ++i) acc[j][i] = Mfma16<T>::mma(wf[u][j], xf[u][i], acc[j][i]);
+  };
+  const int nbat = (k1 - k0) / U;
+  int kt = k0;
+  if constexpr (PIPE) {
+    if (nbat > 0) load(wa, xa, kt);
+    for (int b = 0; b < nbat; b += 2) {
+      if (b + 1 < nbat) load(wb, xb, kt + U);
+      compute(wa, xa);
+      if (b + 1 < nbat) {
+        if (b + 2 < nbat) load(wa, xa, kt + 2 * U);
+        compute(wb, xb);
+      }
+      kt += 2 * U;
+    }
+  } else {
+    // one register set (fewer VGPRs, several workgroups resident per CU); the
+    // activation loads are skipped for m-tiles past the last one (measured
+    // faster here than the clamped form)
+    const Frag16* xp = a.X + (size_t)mt0 * a.KT * 64 + lane;
+    for (int b = 0; b < nbat; ++b, kt += U) {
+      Frag16 wf[U][NT], xf[U][MT];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) wf[u][j] = __builtin_nontemporal_load(&wp[((size_t)j * a.KT + kt + u) * 64]);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
         for (int i = 0; i < MT; ++i)
-          if (i < nmt) acc[j][i] = Mfma16<T>::mma(wf[u][j], xf[u][i], acc[j][i]);
+          if (i < nmt) xf[u][i] = xp[((size_t)i * a.KT + kt + u) * 64];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+            if (i < nmt) acc[j][i] = Mfma16<T>::mma(wf[u][j], xf[u][i], acc[j][i]);
+    }
   }
-  for (; kt < k1; ++kt) {
-    Frag16 wf[NT];
+  for (kt = k0 + nbat * U; kt < k1; ++kt) {
+    Frag16 wf[NT], xf[MT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) wf[j] = __builtin_nontemporal_load(&wp[((size_t)j * a.KT + kt) * 64]);
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
-      if (i < nmt) {
-        const Frag16 xf = xp[((size_t)i * a.KT + kt) * 64];
+    for (int i = 0; i < MT; ++i) xf[i] = xq[i][(size_t)kt * 64];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) acc[j][i] = Mfma16<T>::mma(wf[j], xf, acc[j][i]);
-      }
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int i = 0; i < MT; ++i) acc[j][i] = Mfma16<T>::mma(wf[j], xf[i], acc[j][i]);
   }
 
   // per-wave sums of squares (tiles past the prefetched ones, for K > 4096,
@@ -313,10 +358,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmArgs a, Epi ep
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
     float s = 0.f;
-#pragma unroll
-    for (int q = 0; q < QS; ++q) s += ssv[i][q];
     const int m = (mt0 + i) * 16 + (lane & 15);
-    if (a.ssq && i < nmt && m < a.ssq_ld)
+    const bool row_ok = a.ssq && i < nmt && m < a.ssq_ld;
+#pragma unroll
+    for (int q = 0; q < QS; ++q) s += (row_ok && t_first + q * 4 * NW < a.ssq_tiles) ? ssv[i][q] : 0.f;
+    if (row_ok)
       for (int t = t_first + QS * 4 * NW; t < a.ssq_tiles; t += 4 * NW) s += a.ssq[(size_t)t * a.ssq_ld + m];
     s += __shfl_xor(s, 16);
     s += __shfl_xor(s, 32);
