@@ -37,9 +37,16 @@ def parse():
     p.add_argument("--batch", type=int, default=0, help="override the workload batch")
     p.add_argument("--cache", default="", help="override the cache mode")
     p.add_argument("--rule", default="", help="override the rule")
-    p.add_argument("--cpu-steps", type=int, default=2, help="oracle denoising steps timed for cpu_baseline")
+    p.add_argument("--cpu-steps", type=int, default=16, help="oracle denoising steps timed for cpu_baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--probe", type=int, default=0, metavar="STEPS",
+                   help="counter-collection mode: one cache pass, STEPS denoising steps of block 0 and a "
+                        "copy of COPY_MIB MiB (read once, written once) that calibrates the byte counters; "
+                        "prints one JSON line describing what ran")
     return p.parse_args()
+
+
+COPY_MIB = 256
 
 
 def log(msg):
@@ -87,6 +94,9 @@ def main():
     prompt = gen_prompt(shape, w.batch, w.prompt_len, w.prompt_seed)
     target, alpha = gen_bias(shape, w.batch, w.gen_len, w.bias_seed, w.alpha_max)
     cfg = Engine.cfg_from_workload(w)
+    if args.probe:
+        probe(eng, w, prompt, target, alpha, args.probe, dev)
+        return
     canvases = [eng.canvas(prompt, target, alpha, w.gen_len) for _ in range(args.warmup + args.steps)]
 
     # warmup; the warmup decodes also time every kernel class
@@ -153,6 +163,30 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, host_weights, w, prompt, target, alpha, args.cpu_steps)
     print(json.dumps(out), flush=True)
+
+
+def probe(eng, w, prompt, target, alpha, n_steps, dev):
+    """A short, fixed sequence of launches for hardware-counter runs: the
+    block-0 cache pass, n_steps denoising steps, then torch.neg over a
+    float32 tensor of COPY_MIB MiB (a plain streaming kernel that reads and
+    writes exactly that many bytes once each)."""
+    import torch
+
+    from diffusion_lm_decoding_amd.engine import Engine
+    cfg = Engine.cfg_from_workload(w)
+    cv = eng.canvas(prompt, target, alpha, w.gen_len)
+    eng.refresh(cv, cfg, 0)
+    for _ in range(n_steps):
+        eng.step(cv, cfg, 0)
+    n = COPY_MIB * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize(dev)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize(dev)
+    print(json.dumps({"probe": w.name, "denoising_steps": n_steps, "copy_bytes_read": n * 4,
+                      "copy_bytes_written": n * 4}), flush=True)
+    eng.close()
 
 
 def cpu_baseline(shape, weights, w, prompt, target, alpha, n_steps):

@@ -8,13 +8,19 @@
 // diffusion (prompt queries: the prompt length).
 //
 // One workgroup owns (sequence, head, 32 queries) and a contiguous share of the
-// key tiles; its 4 waves take alternate 32-key tiles.  Per tile a wave computes
-// S^T = K Q^T with MFMA (keys on rows, the 32 queries on columns: lane l owns
-// query l%32), updates an online softmax in log2 units, and multiplies P V with
-// MFMA while P stays in registers: the V^T fragment is read with the key
-// permutation that matches the accumulator layout of S^T.  Wave states are
-// merged in LDS, key shares through a workspace read back in share order by
-// the last-arriving workgroup; the merge order is fixed.
+// key tiles; its NW waves take the share's 32-key tiles round-robin.  Per tile a
+// wave computes S^T = K Q^T with MFMA (keys on rows, the 32 queries on columns:
+// lane l owns query l%32), updates an online softmax in log2 units, and
+// multiplies P V with MFMA while P stays in registers: the V^T fragment is read
+// with the key permutation that matches the accumulator layout of S^T.  The
+// wave states are merged pairwise in LDS (a fixed binary tree).  With several
+// key shares each workgroup writes its state to a workspace and
+// attn_merge_kernel, launched next on the same stream, combines the shares in
+// share order.  (Letting the last-arriving workgroup combine them instead
+// needs an agent-scope release/acquire pair per workgroup, i.e. an L2
+// write-back and invalidate on every XCD; measured slower on MI355X than the
+// second launch.)  Every merge order is fixed, so results are run-to-run
+// identical.
 //
 // Cache layouts: K [batch][H][seq_pad][dh] (head dims in the rotary pair order
 // of the projection), V^T [batch][H][dh][seq_pad].
@@ -44,8 +50,24 @@ __device__ __forceinline__ int attn_limit(const AttnArgs& a, int pos) {
   return a.P + ((pos - a.P) / a.blk + 1) * a.blk;
 }
 
-template <typename T, int DH>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+// Online-softmax states (m, l, o) of the same queries over disjoint keys:
+// (m1, l1, o1) <- their combination.
+template <int ND>
+__device__ __forceinline__ void attn_combine(float& m1, float& l1, f32x16 (&o1)[ND], float m2, float l2,
+                                             const float (*o2)[16][64], int lane) {
+  const float M = fmaxf(m1, m2);
+  const float Ms = M == -INFINITY ? 0.f : M;
+  const float f1 = exp2f(m1 - Ms), f2 = exp2f(m2 - Ms);
+  l1 = l1 * f1 + l2 * f2;
+  m1 = M;
+#pragma unroll
+  for (int i = 0; i < ND; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o1[i][r] = o1[i][r] * f1 + o2[i][r][lane] * f2;
+}
+
+template <typename T, int DH, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   constexpr int KF = Mfma32<T>::KF;
   constexpr int NQF = DH / KF;   // fragments along dh
   constexpr int ND = DH / 32;    // output d-tiles
@@ -88,7 +110,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
 
-  for (int t = t0 + wave; t < t1; t += 4) {
+  for (int t = t0 + wave; t < t1; t += NW) {
     const int kb = t * 32;
     f32x16 s;
 #pragma unroll
@@ -172,69 +194,55 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
   }
 
-  // merge the four waves (fixed order 0, 1, 2, 3)
-  __shared__ float sm_m[4][64], sm_l[4][64];
-  __shared__ float sm_o[3][ND][16][64];
-  sm_m[wave][lane] = mrun;
-  sm_l[wave][lane] = lrun;
-  if (wave > 0) {
+  // merge the waves: round k folds waves [h, 2h) into [0, h), h = NW/2, ..., 1
+  if constexpr (NW > 1) {
+    __shared__ float sm_m[NW / 2][64], sm_l[NW / 2][64];
+    __shared__ float sm_o[NW / 2][ND][16][64];
 #pragma unroll
-    for (int i = 0; i < ND; ++i)
+    for (int half = NW / 2; half >= 1; half /= 2) {
+      if (wave >= half && wave < 2 * half) {
+        const int sl = wave - half;
+        sm_m[sl][lane] = mrun;
+        sm_l[sl][lane] = lrun;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sm_o[wave - 1][i][r][lane] = o[i][r];
+        for (int i = 0; i < ND; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sm_o[sl][i][r][lane] = o[i][r];
+      }
+      __syncthreads();
+      if (wave < half) attn_combine<ND>(mrun, lrun, o, sm_m[wave][lane], sm_l[wave][lane], sm_o[wave], lane);
+      if (half > 1) __syncthreads();
+    }
   }
-  __syncthreads();
-  if (wave != 0) return;
-  float M = mrun;
-#pragma unroll
-  for (int w = 1; w < 4; ++w) M = fmaxf(M, sm_m[w][lane]);
-  const float Ms = M == -INFINITY ? 0.f : M;
-  float L = 0.f;
-  {
-    const float f0 = exp2f(mrun - Ms);
-    L = lrun * f0;
-#pragma unroll
-    for (int i = 0; i < ND; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][r] *= f0;
-  }
-#pragma unroll
-  for (int w = 1; w < 4; ++w) {
-    const float f = exp2f(sm_m[w][lane] - Ms);
-    L += sm_l[w][lane] * f;
-#pragma unroll
-    for (int i = 0; i < ND; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][r] += sm_o[w - 1][i][r][lane] * f;
-  }
-
-  if (a.splits > 1) {
-    const size_t rec = (size_t)(ND * 16 + 2) * 64;
-    float* dst = a.ws + ((size_t)split * gridDim.x + wg) * rec;
-    dst[lane] = M;
-    dst[64 + lane] = L;
-#pragma unroll
-    for (int i = 0; i < ND; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dst[128 + (i * 16 + r) * 64 + lane] = o[i][r];
-    return;  // attn_merge_kernel combines the key shares
-  }
-
-  if (!valid) return;
-  const float inv = 1.0f / L;
   T* out = static_cast<T*>(a.out);
+
+  if (a.splits == 1) {
+    if (wave != 0 || !valid) return;
+    const float inv = 1.0f / lrun;
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        out[packed_off<T>(m, h * DH + i * 32 + acc32_row(r, lane), a.d)] = Elem<T>::cvt(o[i][r] * inv);
+    return;
+  }
+
+  // key shares: this share's state goes to the workspace
+  if (wave != 0) return;
+  const size_t rec = (size_t)(ND * 16 + 2) * 64;
+  float* dst = a.ws + ((size_t)split * gridDim.x + wg) * rec;
+  dst[lane] = mrun;
+  dst[64 + lane] = lrun;
 #pragma unroll
   for (int i = 0; i < ND; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      out[packed_off<T>(m, h * DH + i * 32 + acc32_row(r, lane), a.d)] = Elem<T>::cvt(o[i][r] * inv);
+    for (int r = 0; r < 16; ++r) dst[128 + (i * 16 + r) * 64 + lane] = o[i][r];
 }
 
-// Combine the key shares of a split attention launch in share order (one wave
-// per (sequence, head, 32 queries)); launched after attn_kernel on the same
-// stream, so every share is complete.
-// 256 threads: thread t handles accumulator lane t%64 and the registers
-// (i, r) with (16 i + r) % 4 == t/64.
+// Combine the key shares of a split attention launch in share order (one
+// workgroup per (sequence, head, 32 queries)); launched after attn_kernel on
+// the same stream, so every share is complete.  256 threads: thread t handles
+// accumulator lane t%64 and the registers (i, r) with (16 i + r) % 4 == t/64.
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int nwg) {
   constexpr int ND = DH / 32;

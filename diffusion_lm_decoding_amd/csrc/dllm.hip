@@ -2,6 +2,7 @@
 // model forward over a set of canvas rows, the block step, the cache passes
 // and the host block loop (Fast-dLLM reading notes, Algorithm 1).
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <chrono>
 #include <cmath>
@@ -91,11 +92,14 @@ struct dllm_ctx {
   float* attn_ws = nullptr;
   size_t attn_ws_floats = 0;
 
-  int* d_err = nullptr;       // [0] numeric error, [1] canvas check
-  int* d_ncommit = nullptr;   // [max_batch]
-  int* d_done = nullptr;
+  // one device status block [ncommit(max_batch) | done(max_batch) | err(4)],
+  // read back by a single copy per step into h_pin (same layout)
+  int* d_stat = nullptr;
+  int* d_err = nullptr;       // d_stat + 2 max_batch: [0] numeric error, [1] canvas check
+  int* d_ncommit = nullptr;   // d_stat
+  int* d_done = nullptr;      // d_stat + max_batch
   int* d_step = nullptr;
-  int* h_pin = nullptr;       // pinned: ncommit[max_batch], done[max_batch], err[2]
+  int* h_pin = nullptr;       // pinned copy of the status block
 
   // kernel timing (dllm_set_timing): event pairs pending until the next read
   struct Pending { int cls; hipEvent_t a, b; double bytes, flops; };
@@ -163,24 +167,33 @@ dllm_status check_launch() {
   return DLLM_OK;
 }
 
-// Events around one launch when its class is being timed.
+// Timing of one launch when its class is being timed.  With ext = true the
+// caller passes (a, b) to hipExtLaunchKernelGGL, which stamps them from the
+// kernel's own dispatch packet (kernel duration only); otherwise a and b are
+// recorded on the stream around the launch(es).
 struct Timed {
   dllm_ctx* c;
   int cls;
   double bytes, flops;
-  hipEvent_t a = nullptr;
-  Timed(dllm_ctx* c_, int cls_, double by, double fl) : c(c_), cls(cls_), bytes(by), flops(fl) {
+  bool ext;
+  hipEvent_t a = nullptr, b = nullptr;
+  Timed(dllm_ctx* c_, int cls_, double by, double fl, bool ext_ = false)
+      : c(c_), cls(cls_), bytes(by), flops(fl), ext(ext_) {
     if ((c->timing_mask >> cls) & 1u) {
       a = c->get_event();
-      if (a) (void)hipEventRecord(a, c->stream);
+      b = c->get_event();
+      if (!a || !b) a = b = nullptr;  // reported by done()
+      else if (!ext) (void)hipEventRecord(a, c->stream);
     }
   }
   dllm_status done() {
     TRY(check_launch());
-    if (!a) return DLLM_OK;
-    hipEvent_t b = c->get_event();
-    if (!b) return fail(DLLM_ERR_DEVICE, "hipEventCreate failed");
-    HIPCHK(hipEventRecord(b, c->stream));
+    if ((c->timing_mask >> cls) & 1u) {
+      if (!a) return fail(DLLM_ERR_DEVICE, "hipEventCreate failed");
+    } else {
+      return DLLM_OK;
+    }
+    if (!ext) HIPCHK(hipEventRecord(b, c->stream));
     c->pending.push_back({cls + c->timing_slot, a, b, bytes, flops});
     if (c->pending.size() >= 4096) {
       HIPCHK(hipStreamSynchronize(c->stream));
@@ -239,20 +252,24 @@ double gemm_out_bytes(int cls, int M, int N, int es) {
 // tiles; NT = 2 when that still leaves a multiple of 256 workgroups or very
 // many of them.  Larger M goes to the LDS-tiled kernel.
 template <typename T, int MT, int NT, int U, class Epi>
-dllm_status launch_skinny(dllm_ctx* c, const GemmArgs& a, const Epi& epi) {
+dllm_status launch_skinny(dllm_ctx* c, const Timed& tm, const GemmArgs& a, const Epi& epi) {
   const unsigned grid = (unsigned)((a.n_tiles / NT) * a.m_groups);
   if (grid <= 256)
-    hipLaunchKernelGGL((gemm_skinny_kernel<T, MT, NT, 8, Epi, U, true>), dim3(grid), dim3(512), 0, c->stream, a, epi);
+    hipExtLaunchKernelGGL((gemm_skinny_kernel<T, MT, NT, 8, Epi, U, true>), dim3(grid), dim3(512), 0, c->stream,
+                          tm.a, tm.b, 0, a, epi);
   else
-    hipLaunchKernelGGL((gemm_skinny_kernel<T, MT, NT, 8, Epi, U, false>), dim3(grid), dim3(512), 0, c->stream, a, epi);
+    hipExtLaunchKernelGGL((gemm_skinny_kernel<T, MT, NT, 8, Epi, U, false>), dim3(grid), dim3(512), 0, c->stream,
+                          tm.a, tm.b, 0, a, epi);
   return DLLM_OK;
 }
 
-// n-tiles per workgroup: the largest NT whose grid is either one partial
-// round (192..256 workgroups) or whole rounds of 256 (measured on MI355X for
-// the LLaDA-8B shapes); very wide outputs take NT = 2.
+// n-tiles per workgroup: exactly one round of 256 workgroups when N/16 is 256,
+// 512, 768 or 1024 (measured best on MI355X for the LLaDA-8B shapes: every CU
+// streams one contiguous weight slice); otherwise the largest NT whose grid
+// is one partial round (192..256 workgroups) or whole rounds of 256; very
+// wide outputs take NT = 2.
 template <typename T, int MT, class Epi>
-dllm_status launch_skinny_nt(dllm_ctx* c, const GemmArgs& a, const Epi& epi) {
+dllm_status launch_skinny_nt(dllm_ctx* c, const Timed& tm, const GemmArgs& a, const Epi& epi) {
   auto fits = [&](int nt) {
     if (a.n_tiles % nt) return false;
     const int g = a.n_tiles / nt;
@@ -260,11 +277,12 @@ dllm_status launch_skinny_nt(dllm_ctx* c, const GemmArgs& a, const Epi& epi) {
   };
   // U (fragments per pipelined batch) keeps both register sets in VGPRs
   if constexpr (MT <= 2) {
-    if (fits(4)) return launch_skinny<T, MT, 4, 2>(c, a, epi);
+    if (a.n_tiles == 3 * 256) return launch_skinny<T, MT, 3, 2>(c, tm, a, epi);
+    if (a.n_tiles == 4 * 256 || (a.n_tiles != 2 * 256 && fits(4))) return launch_skinny<T, MT, 4, 2>(c, tm, a, epi);
   }
   if (fits(2) || (a.n_tiles % 2 == 0 && a.n_tiles / 2 >= 2048))
-    return launch_skinny<T, MT, 2, (MT <= 2 ? 4 : 2)>(c, a, epi);
-  return launch_skinny<T, MT, 1, 4>(c, a, epi);
+    return launch_skinny<T, MT, 2, (MT <= 2 ? 4 : 2)>(c, tm, a, epi);
+  return launch_skinny<T, MT, 1, 4>(c, tm, a, epi);
 }
 
 // ssq (optional): partial sums of squares [K/16][ssq_ld] of the input rows;
@@ -284,16 +302,18 @@ dllm_status launch_gemm(dllm_ctx* c, int cls, const void* X, const void* W, int 
   a.inv_k = 1.0f / (float)K;
   a.eps = c->cfg.rms_eps;
   const double es = sizeof(T);
-  Timed tm(c, cls, es * ((double)N * K + (double)M * K) + gemm_out_bytes(cls, M, N, (int)es), 2.0 * M * N * K);
+  Timed tm(c, cls, es * ((double)N * K + (double)M * K) + gemm_out_bytes(cls, M, N, (int)es), 2.0 * M * N * K,
+           /*ext=*/true);
   if (a.m_tiles <= 4) {
     a.m_groups = 1;
-    if (a.m_tiles == 1) TRY((launch_skinny_nt<T, 1>(c, a, epi)));
-    else if (a.m_tiles == 2) TRY((launch_skinny_nt<T, 2>(c, a, epi)));
-    else TRY((launch_skinny_nt<T, 4>(c, a, epi)));
+    if (a.m_tiles == 1) TRY((launch_skinny_nt<T, 1>(c, tm, a, epi)));
+    else if (a.m_tiles == 2) TRY((launch_skinny_nt<T, 2>(c, tm, a, epi)));
+    else TRY((launch_skinny_nt<T, 4>(c, tm, a, epi)));
   } else {
     const int n_wg = cdiv(a.n_tiles, 8), m_wg = cdiv(a.m_tiles, 8);
     a.m_groups = m_wg;
-    hipLaunchKernelGGL((gemm_tiled_kernel<T, Epi>), dim3((unsigned)(n_wg * m_wg)), dim3(256), 0, c->stream, a, epi);
+    hipExtLaunchKernelGGL((gemm_tiled_kernel<T, Epi>), dim3((unsigned)(n_wg * m_wg)), dim3(256), 0, c->stream,
+                          tm.a, tm.b, 0, a, epi);
   }
   return tm.done();
 }
@@ -345,7 +365,7 @@ dllm_status launch_attn(dllm_ctx* c, int layer, const Fwd& f) {
   }
   const double M = (double)f.batch * f.nr;
   Timed tm(c, DLLM_K_ATTN, f.batch * m.n_heads * kv + 2.0 * M * m.d_model * sizeof(T), f.batch * m.n_heads * fl);
-  hipLaunchKernelGGL((attn_kernel<T, DH>), dim3(nwg, splits), dim3(256), 0, c->stream, a);
+  hipLaunchKernelGGL((attn_kernel<T, DH, 4>), dim3(nwg, splits), dim3(256), 0, c->stream, a);
   if (splits > 1) hipLaunchKernelGGL((attn_merge_kernel<T, DH>), dim3(nwg), dim3(256), 0, c->stream, a, nwg);
   return tm.done();
 }
@@ -452,13 +472,13 @@ dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, in
   f.head_off = s - f.row_start;
   TRY(forward<T>(c, f));
   EpiLMHead eh{HR, B, d->gen_len, s - d->prompt_len, cv->bias_target, cv->bias_alpha, m.mask_id, m.vocab,
-               c->pmax, c->psum, c->parg, dbg_logits};
+               c->n_vtiles, c->pmax, c->psum, c->parg, dbg_logits};
   hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, c->stream, c->d_err, 2, 0);
   TRY(check_launch());
   TRY(launch_gemm<T>(c, DLLM_K_LMHEAD, c->xh, c->wlm, HR, m.vocab, m.d_model, eh, c->ssq_head, HR));
   {
     Timed tm(c, DLLM_K_MERGE, 12.0 * c->n_vtiles * HR + 8.0 * HR, 3.0 * c->n_vtiles * HR);
-    hipLaunchKernelGGL(lm_merge_kernel, dim3(HR), dim3(256), 0, c->stream, c->pmax, c->psum, c->parg, c->n_vtiles,
+    hipLaunchKernelGGL(lm_merge_kernel, dim3(HR), dim3(kMergeThreads), 0, c->stream, c->pmax, c->psum, c->parg, c->n_vtiles,
                        HR, c->conf, c->tok, c->d_err);
     TRY(tm.done());
   }
@@ -489,9 +509,7 @@ dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, in
     TRY(tm.done());
   }
   const int mb = c->cfg.max_batch;
-  HIPCHK(hipMemcpyAsync(c->h_pin, c->d_ncommit, d->batch * sizeof(int), hipMemcpyDeviceToHost, c->stream));
-  HIPCHK(hipMemcpyAsync(c->h_pin + mb, c->d_done, d->batch * sizeof(int), hipMemcpyDeviceToHost, c->stream));
-  HIPCHK(hipMemcpyAsync(c->h_pin + 2 * mb, c->d_err, sizeof(int), hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(hipMemcpyAsync(c->h_pin, c->d_stat, (2 * (size_t)mb + 1) * sizeof(int), hipMemcpyDeviceToHost, c->stream));
   HIPCHK(hipStreamSynchronize(c->stream));
   if (c->h_pin[2 * mb]) return fail(DLLM_ERR_NUMERIC, "non-finite logits or confidence in the LM head");
   for (int b = 0; b < d->batch; ++b) {
@@ -588,9 +606,10 @@ dllm_status init_impl(dllm_ctx* c, const void* const* t) {
   TRY(c->alloc(&c->tok, (size_t)c->max_head * sizeof(int)));
   c->attn_ws_floats = (size_t)16 << 20;
   TRY(c->alloc(&c->attn_ws, c->attn_ws_floats * sizeof(float)));
-  TRY(c->alloc(&c->d_err, 4 * sizeof(int)));
-  TRY(c->alloc(&c->d_ncommit, (size_t)m.max_batch * sizeof(int)));
-  TRY(c->alloc(&c->d_done, (size_t)m.max_batch * sizeof(int)));
+  TRY(c->alloc(&c->d_stat, (2 * (size_t)m.max_batch + 4) * sizeof(int)));
+  c->d_ncommit = c->d_stat;
+  c->d_done = c->d_stat + m.max_batch;
+  c->d_err = c->d_stat + 2 * m.max_batch;
   TRY(c->alloc(&c->d_step, (size_t)m.max_batch * sizeof(int)));
   HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&c->h_pin), (2 * m.max_batch + 4) * sizeof(int), hipHostMallocDefault));
   HIPCHK(hipStreamSynchronize(c->stream));

@@ -161,7 +161,8 @@ struct EpiLMHead {
   const int* target;      // may be null
   const float* alpha;
   int mask_id, vocab;
-  float* pmax;            // [n_tiles][M]
+  int n_tiles;            // vocab / 16
+  float* pmax;            // [M][n_tiles]: each row's partials contiguous for the merge
   float* psum;
   int* parg;
   float* dbg;             // [M][vocab] or null
@@ -200,9 +201,9 @@ struct EpiLMHead {
     s += __shfl_xor(s, 16);
     s += __shfl_xor(s, 32);
     if (valid && lane < 16) {
-      pmax[(size_t)nt * M + m] = mx;
-      psum[(size_t)nt * M + m] = s;
-      parg[(size_t)nt * M + m] = am;
+      pmax[(size_t)m * n_tiles + nt] = mx;
+      psum[(size_t)m * n_tiles + nt] = s;
+      parg[(size_t)m * n_tiles + nt] = am;
     }
   }
 };

@@ -55,37 +55,58 @@ __global__ __launch_bounds__(256) void embed_kernel(const int* tokens, int seq_l
 
 // ---- LM-head merge: per row, combine the vocab-tile partials ---------------
 // max and argmax (lowest index among equal maxima), then
-// S = sum_t s_t exp(m_t - max); confidence = 1 / S.
-__global__ __launch_bounds__(256) void lm_merge_kernel(const float* pmax, const float* psum,
-                                                       const int* parg, int n_tiles, int M,
-                                                       float* conf, int* tok, int* err) {
-  __shared__ float shm[256];
-  __shared__ int sha[256];
-  __shared__ float shs[4];
-  const int m = blockIdx.x, t0 = threadIdx.x;
+// S = sum_t s_t exp(m_t - max); confidence = 1 / S.  Partials are [M][n_tiles];
+// one workgroup of kMergeThreads per row.  Each thread keeps its first
+// kMergePer tiles in registers (every load issued before the first use), so
+// the second pass re-reads memory only for vocabularies beyond
+// kMergeThreads * kMergePer tiles.  Reduction orders are fixed.
+constexpr int kMergeThreads = 1024, kMergePer = 8;
+
+__device__ __forceinline__ void argmax_take(float& mx, int& am, float v, int a) {
+  if (v > mx || (v == mx && a < am)) { mx = v; am = a; }
+}
+
+__global__ __launch_bounds__(kMergeThreads) void lm_merge_kernel(const float* pmax, const float* psum,
+                                                                 const int* parg, int n_tiles, int M,
+                                                                 float* conf, int* tok, int* err) {
+  (void)M;
+  constexpr int NWV = kMergeThreads / 64;
+  __shared__ float shm[NWV];
+  __shared__ int sha[NWV];
+  __shared__ float shs[NWV];
+  const int m = blockIdx.x, t0 = threadIdx.x, lane = t0 & 63, wv = t0 >> 6;
+  const float* rmax = pmax + (size_t)m * n_tiles;
+  const float* rsum = psum + (size_t)m * n_tiles;
+  const int* rarg = parg + (size_t)m * n_tiles;
+  float vm[kMergePer], vs[kMergePer];
+  int va[kMergePer];
+#pragma unroll
+  for (int j = 0; j < kMergePer; ++j) {
+    const int t = min(t0 + j * kMergeThreads, n_tiles - 1);
+    vm[j] = rmax[t];
+    va[j] = rarg[t];
+    vs[j] = rsum[t];
+  }
   float mx = -INFINITY;
   int am = 0x7fffffff;
-  for (int t = t0; t < n_tiles; t += 256) {
-    const float v = pmax[(size_t)t * M + m];
-    const int a = parg[(size_t)t * M + m];
-    if (v > mx || (v == mx && a < am)) { mx = v; am = a; }
-  }
-  shm[t0] = mx;
-  sha[t0] = am;
+#pragma unroll
+  for (int j = 0; j < kMergePer; ++j)
+    if (t0 + j * kMergeThreads < n_tiles) argmax_take(mx, am, vm[j], va[j]);
+  for (int t = t0 + kMergePer * kMergeThreads; t < n_tiles; t += kMergeThreads) argmax_take(mx, am, rmax[t], rarg[t]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) argmax_take(mx, am, __shfl_xor(mx, o), __shfl_xor(am, o));
+  if (lane == 0) { shm[wv] = mx; sha[wv] = am; }
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (t0 < s) {
-      const float v = shm[t0 + s];
-      const int a = sha[t0 + s];
-      if (v > shm[t0] || (v == shm[t0] && a < sha[t0])) { shm[t0] = v; sha[t0] = a; }
-    }
-    __syncthreads();
-  }
-  const float gm = shm[0];
-  const int ga = sha[0];
+  float gm = shm[0];
+  int ga = sha[0];
+#pragma unroll
+  for (int w = 1; w < NWV; ++w) argmax_take(gm, ga, shm[w], sha[w]);
   float s = 0.f;
-  for (int t = t0; t < n_tiles; t += 256) s += psum[(size_t)t * M + m] * expf(pmax[(size_t)t * M + m] - gm);
-  s = block_sum<256>(s, shs);
+#pragma unroll
+  for (int j = 0; j < kMergePer; ++j)
+    if (t0 + j * kMergeThreads < n_tiles) s += vs[j] * expf(vm[j] - gm);
+  for (int t = t0 + kMergePer * kMergeThreads; t < n_tiles; t += kMergeThreads) s += rsum[t] * expf(rmax[t] - gm);
+  s = block_sum<kMergeThreads>(s, shs);
   if (t0 == 0) {
     conf[m] = 1.0f / s;
     tok[m] = ga;
