@@ -24,6 +24,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# HBM bytes per launch of the dominant kernel from two rocprofv3 --pmc runs
+# (FETCH_SIZE, WRITE_SIZE, calibrated on a copy of known size), valid only
+# while the kernel sources hash to the value recorded with them
+TRAFFIC_PROFILES = {("llada8b_p512_g256", "gateup"): "profiles/gateup_projection_llada8b_p512_g256.md"}
 # dense MFMA peaks (TFLOP/s): fp16/bf16 inputs, fp32 inputs
 PEAKS_TFLOPS = {"f16": 2500.0, "f32": 157.3}
 
@@ -132,7 +136,9 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": kt["flops"] / kt["ms"] / 1e9, "peak": PEAKS_TFLOPS[dtype],
                 "unit": "TFLOP/s"}
-    roof.update(frac=roof["achieved"] / roof["peak"], traffic=None, kernel=f"{dom} projection (denoising step)",
+    roof.update(frac=roof["achieved"] / roof["peak"], traffic=stored_traffic(w.name, dom),
+                traffic_unit="HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                kernel=f"{dom} projection (denoising step)",
                 launches=kt["launches"], us_per_launch=1e3 * kt["ms"] / n,
                 bytes_per_launch=kt["bytes"] / n, flops_per_launch=kt["flops"] / n)
 
@@ -187,6 +193,30 @@ def probe(eng, w, prompt, target, alpha, n_steps, dev):
     print(json.dumps({"probe": w.name, "denoising_steps": n_steps, "copy_bytes_read": n * 4,
                       "copy_bytes_written": n * 4}), flush=True)
     eng.close()
+
+
+def stored_traffic(workload, cls):
+    """Measured HBM bytes per launch recorded for (workload, kernel class), or
+    None when there is no record or the kernel sources changed since."""
+    import hashlib
+    rel = TRAFFIC_PROFILES.get((workload, cls))
+    if rel is None or not os.path.exists(os.path.join(ROOT, rel)):
+        return None
+    fields = {}
+    for line in open(os.path.join(ROOT, rel)):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip()
+    try:
+        h = hashlib.sha256()
+        for f in fields["sources"].split(","):
+            with open(os.path.join(ROOT, f.strip()), "rb") as fh:
+                h.update(fh.read())
+        if h.hexdigest() != fields["sources_sha256"]:
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
 
 
 def cpu_baseline(shape, weights, w, prompt, target, alpha, n_steps):
