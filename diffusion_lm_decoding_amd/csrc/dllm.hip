@@ -89,6 +89,8 @@ struct dllm_ctx {
   int* tok = nullptr;
   float* ssq = nullptr;       // [d/16][max_rows] partial sums of x^2 of the residual rows
   float* ssq_head = nullptr;  // [d/16][max_head] same for the LM-head rows
+  float* rstd = nullptr;      // [rstd_rows] per-row 1/rms for the large-M projections
+  int rstd_rows = 0;
   float* attn_ws = nullptr;
   size_t attn_ws_floats = 0;
 
@@ -285,6 +287,36 @@ dllm_status launch_skinny_nt(dllm_ctx* c, const Timed& tm, const GemmArgs& a, co
   return launch_skinny<T, MT, 1, 4>(c, tm, a, epi);
 }
 
+// Large-M tile shapes (NTW x MTW 16x16 tiles per workgroup), measured on
+// MI355X for the LLaDA-8B cache-pass and batch-16 shapes; eff is the relative
+// throughput of one busy CU.
+struct BigCfg { int ntw, mtw; double eff; };
+constexpr BigCfg kBigCfgs[] = {{12, 12, 1.0}, {16, 8, 0.85}, {8, 8, 0.75}, {8, 6, 0.72}};
+
+template <typename T, class Epi>
+dllm_status launch_big(dllm_ctx* c, const GemmArgs& a, const Epi& epi) {
+  // estimated time ~ rounds of 256 workgroups x tile area / eff
+  int best = 0;
+  double best_t = 1e300;
+  for (int i = 0; i < 4; ++i) {
+    const BigCfg& g = kBigCfgs[i];
+    const double nwg = (double)cdiv(a.n_tiles, g.ntw) * cdiv(a.m_tiles, g.mtw);
+    const double t = std::ceil(nwg / 256.0) * g.ntw * g.mtw / g.eff;
+    if (t < best_t) { best_t = t; best = i; }
+  }
+  const bool ks2 = a.KT % 2 == 0;
+  if (!ks2 && best >= 2) best = -1;  // 8x6 and 8x8 use two k-fragments per stage
+  auto grid = [&](int ntw, int mtw) { return dim3((unsigned)(cdiv(a.n_tiles, ntw) * cdiv(a.m_tiles, mtw))); };
+  switch (best) {
+    case 0: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 12, 12, 2, 4, 1, 4>), grid(12, 12), dim3(512), 0, c->stream, a, epi); break;
+    case 1: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 16, 8, 4, 2, 1, 4>), grid(16, 8), dim3(512), 0, c->stream, a, epi); break;
+    case 2: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 8, 2, 2, 2, 4>), grid(8, 8), dim3(256), 0, c->stream, a, epi); break;
+    case 3: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 6, 2, 2, 2, 4>), grid(8, 6), dim3(256), 0, c->stream, a, epi); break;
+    default: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 8, 2, 2, 1, 6>), grid(8, 8), dim3(256), 0, c->stream, a, epi); break;
+  }
+  return DLLM_OK;
+}
+
 // ssq (optional): partial sums of squares [K/16][ssq_ld] of the input rows;
 // X then holds x * gain and the kernel applies the per-row 1/rms.
 template <typename T, class Epi>
@@ -302,19 +334,23 @@ dllm_status launch_gemm(dllm_ctx* c, int cls, const void* X, const void* W, int 
   a.inv_k = 1.0f / (float)K;
   a.eps = c->cfg.rms_eps;
   const double es = sizeof(T);
-  Timed tm(c, cls, es * ((double)N * K + (double)M * K) + gemm_out_bytes(cls, M, N, (int)es), 2.0 * M * N * K,
-           /*ext=*/true);
+  const double bytes = es * ((double)N * K + (double)M * K) + gemm_out_bytes(cls, M, N, (int)es);
   if (a.m_tiles <= 4) {
+    Timed tm(c, cls, bytes, 2.0 * M * N * K, /*ext=*/true);
     a.m_groups = 1;
     if (a.m_tiles == 1) TRY((launch_skinny_nt<T, 1>(c, tm, a, epi)));
     else if (a.m_tiles == 2) TRY((launch_skinny_nt<T, 2>(c, tm, a, epi)));
     else TRY((launch_skinny_nt<T, 4>(c, tm, a, epi)));
-  } else {
-    const int n_wg = cdiv(a.n_tiles, 8), m_wg = cdiv(a.m_tiles, 8);
-    a.m_groups = m_wg;
-    hipExtLaunchKernelGGL((gemm_tiled_kernel<T, Epi>), dim3((unsigned)(n_wg * m_wg)), dim3(256), 0, c->stream,
-                          tm.a, tm.b, 0, a, epi);
+    return tm.done();
   }
+  Timed tm(c, cls, bytes, 2.0 * M * N * K);
+  if (ssq) {
+    if (ssq_ld > c->rstd_rows) return fail(DLLM_ERR_ARG, "internal: rstd buffer too small");
+    hipLaunchKernelGGL(rstd_kernel, dim3((unsigned)cdiv(ssq_ld, 4)), dim3(256), 0, c->stream, ssq, a.ssq_tiles, ssq_ld,
+                       a.inv_k, a.eps, c->rstd);
+    a.rstd = c->rstd;
+  }
+  TRY((launch_big<T, Epi>(c, a, epi)));
   return tm.done();
 }
 
@@ -598,6 +634,8 @@ dllm_status init_impl(dllm_ctx* c, const void* const* t) {
   TRY(c->alloc(&c->xh, (size_t)c->max_head_pad * d * es));
   TRY(c->alloc(&c->ssq, (size_t)(d / 16) * c->max_rows * sizeof(float)));
   TRY(c->alloc(&c->ssq_head, (size_t)(d / 16) * c->max_head * sizeof(float)));
+  c->rstd_rows = std::max(c->max_rows, c->max_head);
+  TRY(c->alloc(&c->rstd, (size_t)c->rstd_rows * sizeof(float)));
   c->n_vtiles = V / 16;
   TRY(c->alloc(&c->pmax, (size_t)c->n_vtiles * c->max_head * sizeof(float)));
   TRY(c->alloc(&c->psum, (size_t)c->n_vtiles * c->max_head * sizeof(float)));

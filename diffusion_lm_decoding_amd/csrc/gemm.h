@@ -8,9 +8,9 @@
 //    weight fragments straight from HBM once, reuse the activation fragments
 //    across the NT tiles, and add their partial accumulators through LDS in
 //    wave order.  16-wide tiles give N/16 workgroups (256 for N = 4096).
-//  * gemm_tiled_kernel (large M: cache passes, big batches): 4 waves own a
-//    128x128 output tile; fragments of both operands are staged through a
-//    double-buffered LDS ring and shared by the waves.
+//  * gemm_big_kernel (large M: cache passes, big batches): a workgroup owns a
+//    tile of up to 192x192 outputs; fragments of both operands are copied
+//    into a multi-stage LDS ring by the DMA path and shared by the waves.
 #pragma once
 #include "mfma.h"
 
@@ -221,17 +221,10 @@ struct GemmArgs {
   const float* ssq;
   int ssq_tiles, ssq_ld;
   float inv_k, eps;
+  // gemm_big_kernel: per-row 1/rms computed beforehand by rstd_kernel
+  // (required there when ssq is set)
+  const float* rstd;
 };
-
-// 1/rms of row m (lanes with equal m%16 cooperate; every lane gets the result)
-__device__ __forceinline__ float row_rstd(const GemmArgs& a, int m, int lane) {
-  float s = 0.f;
-  if (m < a.ssq_ld)
-    for (int t = lane >> 4; t < a.ssq_tiles; t += 4) s += a.ssq[(size_t)t * a.ssq_ld + m];
-  s += __shfl_xor(s, 16);
-  s += __shfl_xor(s, 32);
-  return 1.0f / sqrtf(s * a.inv_k + a.eps);
-}
 
 // Workgroup i runs on XCD i % 8; map consecutive logical ids to one XCD so the
 // workgroups that share weight tiles share an L2.
@@ -411,96 +404,123 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmArgs a, Epi ep
     for (int i = 0; i < nmt; ++i) epi(nt0 + j, mt0 + i, acc[j][i], lane);
 }
 
-// 128x128 output tile per workgroup of 4 waves (2x2, 64x64 each); BK fragments
-// of both operands per LDS stage, two stages in flight.
-template <typename T, class Epi>
-__global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a, Epi epi) {
-  constexpr int BK = 2;                    // k fragments per stage
-  constexpr int TILES = 8;                 // 16-row tiles per operand per WG
-  constexpr int FR = 2 * TILES * BK;       // fragments per stage (W then X)
-  __shared__ Frag16 lds[2][FR][64];        // 2 x 32 KiB
+// ---------------------------------------------------------------------------
+// Large-M projection (cache passes, big batches).  A workgroup of WN x WM waves
+// owns NTW x MTW 16x16 output tiles.  Operand fragments are copied straight
+// from HBM/L2 into LDS by the DMA path (global_load_lds_dwordx4: 64 lanes x
+// 16 B = one packed fragment per wave instruction, no VGPR staging) through a
+// ring of S stages of KS k-fragments each; S-1 stages are in flight while the
+// MFMAs consume the oldest.  Waits are explicit: vmcnt for this wave's own
+// copies, then s_barrier so every wave's copies of the stage have landed;
+// lgkmcnt(0) before the barrier that hands a stage back to the copier.
+// Out-of-range tiles are clamped to the last valid one (valid memory; their
+// results are discarded by the epilogue guards).
+// ---------------------------------------------------------------------------
+// rstd[m] = 1 / sqrt(sum_t ssq[t][m] / K + eps), one wave per row; the 64
+// lanes take tiles t = lane, lane + 64, ... and add in a fixed tree.
+__global__ __launch_bounds__(256) void rstd_kernel(const float* ssq, int tiles, int ld, float inv_k, float eps,
+                                                   float* rstd) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= ld) return;
+  float s = 0.f;
+  for (int t = lane; t < tiles; t += 64) s += ssq[(size_t)t * ld + m];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) rstd[m] = 1.0f / sqrtf(s * inv_k + eps);
+}
+
+template <int V>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(V >= 0 && V < 64, "vmcnt range");
+  // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+  __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | (15 << 8) | ((V >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+template <typename T, class Epi, int NTW, int MTW, int WN, int WM, int KS, int S>
+__global__ __launch_bounds__(64 * WN * WM) void gemm_big_kernel(GemmArgs a, Epi epi) {
+  constexpr int NWAVE = WN * WM;
+  constexpr int F = KS * (NTW + MTW);     // fragments per stage
+  constexpr int LW = F / NWAVE;           // copies per wave per stage
+  static_assert(F % NWAVE == 0, "stage fragments must split evenly over the waves");
+  constexpr int TN = NTW / WN, TM = MTW / WM;  // wave tile in 16x16 tiles
+  static_assert(NTW % WN == 0 && MTW % WM == 0, "wave grid must divide the tile");
+  __shared__ Frag16 lds[S][F][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n_wg = (a.n_tiles + TILES - 1) / TILES;
+  const int m_wg = (a.m_tiles + MTW - 1) / MTW;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int wg_n = lin % n_wg, wg_m = lin / n_wg;
-  const int nt0 = wg_n * TILES, mt0 = wg_m * TILES;
-  const int wm = wave >> 1, wn = wave & 1;  // wave's 64x64 quadrant
+  const int wg_m = lin % m_wg, wg_n = lin / m_wg;   // m fastest: neighbours share the weight tile
+  const int nt0 = wg_n * NTW, mt0 = wg_m * MTW;
+  const int wn = wave % WN, wm = wave / WN;
+  const int nst = a.KT / KS;
 
-  // each thread copies FR*64/256 = 8 fragments per stage
-  auto load_stage = [&](int kt, Frag16* regs) {
+  // this wave's copies: fragment f = wave + q * NWAVE of each stage
+  const Frag16* src[LW];
+  int soff[LW];
 #pragma unroll
-    for (int q = 0; q < FR * 64 / 256; ++q) {
-      const int idx = threadIdx.x + 256 * q;       // 0 .. FR*64-1
-      const int f = idx >> 6, l = idx & 63;
-      const int isx = f >= TILES * BK;
-      const int ff = f - isx * TILES * BK;
-      const int tile = ff / BK, kk = ff % BK;
-      const int k = kt + kk;
-      Frag16 v = Frag16{0u, 0u, 0u, 0u};
-      if (!isx) {
-        if (nt0 + tile < a.n_tiles && k < a.KT)
-          v = __builtin_nontemporal_load(&a.W[(((size_t)(nt0 + tile)) * a.KT + k) * 64 + l]);
-      } else {
-        if (mt0 + tile < a.m_tiles && k < a.KT) v = a.X[(((size_t)(mt0 + tile)) * a.KT + k) * 64 + l];
-      }
-      regs[q] = v;
-    }
-  };
-  auto store_stage = [&](int buf, const Frag16* regs) {
+  for (int q = 0; q < LW; ++q) {
+    const int f = wave + q * NWAVE;
+    const bool isw = f < KS * NTW;
+    const int ff = isw ? f : f - KS * NTW;
+    const int tile = ff / KS, kk = ff % KS;
+    const int t = isw ? min(nt0 + tile, a.n_tiles - 1) : min(mt0 + tile, a.m_tiles - 1);
+    src[q] = (isw ? a.W : a.X) + ((size_t)t * a.KT + kk) * 64 + lane;
+    soff[q] = f;
+  }
+  auto issue = [&](int st) {
+    const int buf = st % S;
 #pragma unroll
-    for (int q = 0; q < FR * 64 / 256; ++q) {
-      const int idx = threadIdx.x + 256 * q;
-      lds[buf][idx >> 6][idx & 63] = regs[q];
-    }
+    for (int q = 0; q < LW; ++q)
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src[q] + (size_t)st * KS * 64),
+                                       (__attribute__((address_space(3))) void*)&lds[buf][soff[q]][0], 16, 0, 0);
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[TN][TM];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < TN; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < TM; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  Frag16 regs[FR * 64 / 256];
-  load_stage(0, regs);
-  store_stage(0, regs);
-  __syncthreads();
-  int buf = 0;
-  for (int kt = 0; kt < a.KT; kt += BK) {
-    const bool more = kt + BK < a.KT;
-    if (more) load_stage(kt + BK, regs);
 #pragma unroll
-    for (int kk = 0; kk < BK; ++kk) {
-      Frag16 wf[4], xf[4];
+  for (int st = 0; st < S - 1; ++st)
+    if (st < nst) issue(st);
+  for (int st = 0; st < nst; ++st) {
+    // stage st landed (this wave), then every wave's copies and reads of st-1
+    if (st + S - 2 < nst) wait_vmcnt<(S - 2) * LW>();
+    else wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    if (st + S - 1 < nst) issue(st + S - 1);
+    const int buf = st % S;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wf[j] = lds[buf][(wn * 4 + j) * BK + kk][lane];
+    for (int kk = 0; kk < KS; ++kk) {
+      Frag16 wf[TN], xf[TM];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xf[i] = lds[buf][TILES * BK + (wm * 4 + i) * BK + kk][lane];
+      for (int j = 0; j < TN; ++j) wf[j] = lds[buf][(wn * TN + j) * KS + kk][lane];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int i = 0; i < TM; ++i) xf[i] = lds[buf][KS * NTW + (wm * TM + i) * KS + kk][lane];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[j][i] = Mfma16<T>::mma(wf[j], xf[i], acc[j][i]);
-    }
-    if (more) {
-      store_stage(buf ^ 1, regs);
-      __syncthreads();
-      buf ^= 1;
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int i = 0; i < TM; ++i) acc[j][i] = Mfma16<T>::mma(wf[j], xf[i], acc[j][i]);
     }
   }
   if (a.ssq) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float rs = row_rstd(a, (mt0 + wm * 4 + i) * 16 + (lane & 15), lane);
+    for (int i = 0; i < TM; ++i) {
+      const float rs = a.rstd[min((mt0 + wm * TM + i) * 16 + (lane & 15), a.ssq_ld - 1)];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j][i] *= rs;
+      for (int j = 0; j < TN; ++j) acc[j][i] *= rs;
     }
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int nt = nt0 + wn * 4 + j;
+  for (int j = 0; j < TN; ++j) {
+    const int nt = nt0 + wn * TN + j;
     if (nt >= a.n_tiles) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int mt = mt0 + wm * 4 + i;
+    for (int i = 0; i < TM; ++i) {
+      const int mt = mt0 + wm * TM + i;
       if (mt < a.m_tiles) epi(nt, mt, acc[j][i], lane);
     }
   }
