@@ -8,22 +8,25 @@
 // diffusion (prompt queries: the prompt length).
 //
 // One workgroup owns (sequence, head, 32 queries) and a contiguous share of the
-// key tiles; its NW waves take the share's 32-key tiles round-robin.  Per tile a
-// wave computes S^T = K Q^T with MFMA (keys on rows, the 32 queries on columns:
-// lane l owns query l%32), updates an online softmax in log2 units, and
-// multiplies P V with MFMA while P stays in registers: the V^T fragment is read
-// with the key permutation that matches the accumulator layout of S^T.  The
-// wave states are merged pairwise in LDS (a fixed binary tree).  With several
-// key shares each workgroup writes its state to a workspace and
+// key tiles (shares spread short batches over all CUs); its NW waves take the
+// 32-key tiles round-robin.  Per tile a wave computes S^T = K Q^T with MFMA (keys on rows,
+// the 32 queries on columns: lane l owns query l%32), updates an online
+// softmax in log2 units, and multiplies P V with MFMA while P stays in
+// registers: the V^T fragment holds the keys in the order that matches the
+// accumulator layout of S^T.  The wave states are merged pairwise in LDS (a
+// fixed binary tree).
+//
+// With several key shares each workgroup writes its state to a workspace and
 // attn_merge_kernel, launched next on the same stream, combines the shares in
-// share order.  (Letting the last-arriving workgroup combine them instead
-// needs an agent-scope release/acquire pair per workgroup, i.e. an L2
-// write-back and invalidate on every XCD; measured slower on MI355X than the
-// second launch.)  Every merge order is fixed, so results are run-to-run
-// identical.
+// share order.  (Letting the
+// last-arriving workgroup combine them instead needs an agent-scope
+// release/acquire pair per workgroup, i.e. an L2 write-back and invalidate on
+// every XCD; measured slower on MI355X than the second launch.)  Every merge
+// order is fixed, so results are run-to-run identical.
 //
 // Cache layouts: K [batch][H][seq_pad][dh] (head dims in the rotary pair order
-// of the projection), V^T [batch][H][dh][seq_pad].
+// of the projection), V^T [batch][H][dh][seq_pad] with, for 16-bit types, the
+// keys of each 32-key tile in the order given by vt_col (gemm.h).
 #pragma once
 #include "gemm.h"
 
@@ -66,138 +69,93 @@ __device__ __forceinline__ void attn_combine(float& m1, float& l1, f32x16 (&o1)[
     for (int r = 0; r < 16; ++r) o1[i][r] = o1[i][r] * f1 + o2[i][r][lane] * f2;
 }
 
-template <typename T, int DH, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
-  constexpr int KF = Mfma32<T>::KF;
-  constexpr int NQF = DH / KF;   // fragments along dh
-  constexpr int ND = DH / 32;    // output d-tiles
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int hf = lane >> 5;
-  const int wg = blockIdx.x, split = blockIdx.y;
-  const int qb = wg % a.qblocks, bh = wg / a.qblocks;
-  const int h = bh % a.H, b = bh / a.H;
-
-  const int irow = qb * 32 + (lane & 31);
-  const bool valid = irow < a.g.nr;
-  const int m = b * a.g.nr + (valid ? irow : 0);
-  const int pos = a.g.row_start + (valid ? irow : 0);
-  const int limit = valid ? attn_limit(a, pos) : 0;
-  const int last = min(a.g.nr, qb * 32 + 32) - 1;
-  const int kmax = attn_limit(a, a.g.row_start + last);
-  const int ntile = (kmax + 31) / 32;
-  const int t0 = (int)((long)ntile * split / a.splits), t1 = (int)((long)ntile * (split + 1) / a.splits);
-
-  const T* q = static_cast<const T*>(a.q);
-  const T* kc = static_cast<const T*>(a.kc) + ((size_t)b * a.H + h) * a.seq_pad * DH;
-  const T* vt = static_cast<const T*>(a.vt) + ((size_t)b * a.H + h) * DH * a.seq_pad;
-
-  Frag16 qf[NQF];
-#pragma unroll
-  for (int c = 0; c < NQF; ++c) {
-    const T* src = q + (size_t)m * a.d + h * DH + c * KF;
-    if constexpr (sizeof(T) == 2) {
-      qf[c] = *reinterpret_cast<const Frag16*>(src + 8 * hf);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qf[c][e] = __float_as_uint(reinterpret_cast<const float*>(src)[2 * e + hf]);
-    }
+// Which rows, keys and key tiles a workgroup covers.
+struct AttnWork {
+  int lane, wave, hf, wg, split, h, b;
+  int m, limit;   // this lane's query row and its key limit
+  bool valid;
+  int t0, t1;     // key tiles [t0, t1) of this share
+  __device__ AttnWork(const AttnArgs& a) {
+    lane = threadIdx.x & 63;
+    wave = threadIdx.x >> 6;
+    hf = lane >> 5;
+    wg = blockIdx.x;
+    split = blockIdx.y;
+    const int qb = wg % a.qblocks, bh = wg / a.qblocks;
+    h = bh % a.H;
+    b = bh / a.H;
+    const int irow = qb * 32 + (lane & 31);
+    valid = irow < a.g.nr;
+    m = b * a.g.nr + (valid ? irow : 0);
+    limit = valid ? attn_limit(a, a.g.row_start + irow) : 0;
+    const int last = min(a.g.nr, qb * 32 + 32) - 1;
+    const int ntile = (attn_limit(a, a.g.row_start + last) + 31) / 32;
+    t0 = (int)((long)ntile * split / a.splits);
+    t1 = (int)((long)ntile * (split + 1) / a.splits);
   }
+};
 
-  float mrun = -INFINITY, lrun = 0.f;
-  f32x16 o[ND];
+// S^T = K Q^T for one 32-key tile, online-softmax update, o += P V.
+// kf: K fragments of the tile; for 16-bit types vf holds the V^T fragments
+// (d-tile i, key half c) in vt_col order.
+template <typename T, int DH>
+__device__ __forceinline__ void attn_tile16(const Frag16 (&qf)[DH / 16], const Frag16 (&kf)[DH / 16],
+                                            const Frag16 (&vf)[DH / 32][2], int kb, int limit, float scale_log2,
+                                            float& mrun, float& lrun, f32x16 (&o)[DH / 32], int lane) {
+  constexpr int NQF = DH / 16, ND = DH / 32;
+  f32x16 s;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+  for (int c = 0; c < NQF; ++c) s = Mfma32<T>::mma(kf[c], qf[c], s);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = kb + acc32_row(r, lane);
+    s[r] = key < limit ? s[r] * scale_log2 : -INFINITY;
+    mx = fmaxf(mx, s[r]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mnew = fmaxf(mrun, mx);
+  const float msafe = mnew == -INFINITY ? 0.f : mnew;
+  const float alpha = exp2f(mrun - msafe);
+  float psum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s[r] = exp2f(s[r] - msafe);
+    psum += s[r];
+  }
+  psum += __shfl_xor(psum, 32);
+  lrun = lrun * alpha + psum;
+  mrun = mnew;
 #pragma unroll
   for (int i = 0; i < ND; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
+    for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+  // accumulator register r of S^T holds key kb + acc32_row(r, lane)
+  Frag16 pf[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pf[c][e] = Elem<T>::bits(s[8 * c + 2 * e]) | (Elem<T>::bits(s[8 * c + 2 * e + 1]) << 16);
+#pragma unroll
+  for (int i = 0; i < ND; ++i)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) o[i] = Mfma32<T>::mma(vf[i][c], pf[c], o[i]);
+}
 
-  for (int t = t0 + wave; t < t1; t += NW) {
-    const int kb = t * 32;
-    f32x16 s;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.f;
-    const T* krow = kc + (size_t)(kb + (lane & 31)) * DH;
-    // 16-bit types: the tile's K and V fragments are requested together, so the
-    // V latency hides behind the QK^T products and the softmax
-    Frag16 kf[NQF];
-    Frag16 vf[ND][2];
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int c = 0; c < NQF; ++c) kf[c] = *reinterpret_cast<const Frag16*>(krow + c * KF + 8 * hf);
-#pragma unroll
-      for (int i = 0; i < ND; ++i) {
-        const T* vrow = vt + (size_t)(i * 32 + (lane & 31)) * a.seq_pad + kb + 4 * hf;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 16 * c);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 * c + 8);
-          vf[i][c] = Frag16{lo.x, lo.y, hi.x, hi.y};
-        }
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < NQF; ++c)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) kf[c][e] = __float_as_uint(reinterpret_cast<const float*>(krow)[c * KF + 2 * e + hf]);
-    }
-#pragma unroll
-    for (int c = 0; c < NQF; ++c) s = Mfma32<T>::mma(kf[c], qf[c], s);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kb + acc32_row(r, lane);
-      s[r] = key < limit ? s[r] * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, s[r]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(mrun, mx);
-    const float msafe = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = exp2f(mrun - msafe);
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = exp2f(s[r] - msafe);
-      psum += s[r];
-    }
-    psum += __shfl_xor(psum, 32);
-    lrun = lrun * alpha + psum;
-    mrun = mnew;
-#pragma unroll
-    for (int i = 0; i < ND; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-
-    // P V: the accumulator register r of S^T holds key kb + acc32_row(r, lane)
-    if constexpr (sizeof(T) == 2) {
-      Frag16 pf[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          pf[c][e] = Elem<T>::bits(s[8 * c + 2 * e]) | (Elem<T>::bits(s[8 * c + 2 * e + 1]) << 16);
-#pragma unroll
-      for (int i = 0; i < ND; ++i)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) o[i] = Mfma32<T>::mma(vf[i][c], pf[c], o[i]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < ND; ++i) {
-        const float* vrow = reinterpret_cast<const float*>(vt) + (size_t)(i * 32 + (lane & 31)) * a.seq_pad + kb + 4 * hf;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const Frag16 vf = *reinterpret_cast<const Frag16*>(vrow + 8 * u);
-          Frag16 pf;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) pf[e] = __float_as_uint(s[4 * u + e]);
-          o[i] = Mfma32<T>::mma(vf, pf, o[i]);
-        }
-      }
-    }
-  }
-
-  // merge the waves: round k folds waves [h, 2h) into [0, h), h = NW/2, ..., 1
+// Merge the NW wave states (tree in LDS, lds: >= (NW/2) * (2 + 16 ND) * 64
+// floats, free on entry), then wave 0 writes the normalised output or, with
+// several key shares, the share's state to the workspace.
+template <typename T, int DH, int NW>
+__device__ __forceinline__ void attn_finish(const AttnArgs& a, const AttnWork& w, float mrun, float lrun,
+                                            f32x16 (&o)[DH / 32], float* lds) {
+  constexpr int ND = DH / 32;
+  const int lane = w.lane, wave = w.wave;
   if constexpr (NW > 1) {
-    __shared__ float sm_m[NW / 2][64], sm_l[NW / 2][64];
-    __shared__ float sm_o[NW / 2][ND][16][64];
+    float (*sm_m)[64] = reinterpret_cast<float (*)[64]>(lds);
+    float (*sm_l)[64] = reinterpret_cast<float (*)[64]>(lds + (NW / 2) * 64);
+    float (*sm_o)[ND][16][64] = reinterpret_cast<float (*)[ND][16][64]>(lds + NW * 64);
 #pragma unroll
     for (int half = NW / 2; half >= 1; half /= 2) {
       if (wave >= half && wave < 2 * half) {
@@ -214,29 +172,131 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
       if (half > 1) __syncthreads();
     }
   }
-  T* out = static_cast<T*>(a.out);
-
-  if (a.splits == 1) {
-    if (wave != 0 || !valid) return;
-    const float inv = 1.0f / lrun;
+  if (wave != 0) return;
+  if (a.splits > 1) {
+    const size_t rec = (size_t)(ND * 16 + 2) * 64;
+    float* dst = a.ws + ((size_t)w.split * gridDim.x + w.wg) * rec;
+    dst[lane] = mrun;
+    dst[64 + lane] = lrun;
 #pragma unroll
     for (int i = 0; i < ND; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        out[packed_off<T>(m, h * DH + i * 32 + acc32_row(r, lane), a.d)] = Elem<T>::cvt(o[i][r] * inv);
-    return;
+      for (int r = 0; r < 16; ++r) dst[128 + (i * 16 + r) * 64 + lane] = o[i][r];
+    return;  // attn_merge_kernel combines the key shares
   }
-
-  // key shares: this share's state goes to the workspace
-  if (wave != 0) return;
-  const size_t rec = (size_t)(ND * 16 + 2) * 64;
-  float* dst = a.ws + ((size_t)split * gridDim.x + wg) * rec;
-  dst[lane] = mrun;
-  dst[64 + lane] = lrun;
+  if (!w.valid) return;
+  const float inv = 1.0f / lrun;
+  T* out = static_cast<T*>(a.out);
 #pragma unroll
   for (int i = 0; i < ND; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dst[128 + (i * 16 + r) * 64 + lane] = o[i][r];
+    for (int r = 0; r < 16; ++r)
+      out[packed_off<T>(w.m, w.h * DH + i * 32 + acc32_row(r, lane), a.d)] = Elem<T>::cvt(o[i][r] * inv);
+}
+
+template <int NW, int DH>
+constexpr int attn_merge_floats() { return (NW / 2) * (2 + 16 * (DH / 32)) * 64; }
+
+// Fragments are loaded into registers per tile: with the key shares spread
+// over all CUs each wave holds about one tile, so a deeper copy pipeline has
+// nothing to hide (an LDS-ring variant that streams a whole head through one
+// workgroup measured no faster on MI355X: one CU cannot keep enough bytes in
+// flight to cover the memory latency at this little compute per tile).
+template <typename T, int DH, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
+  constexpr int KF = Mfma32<T>::KF;
+  constexpr int NQF = DH / KF;
+  constexpr int ND = DH / 32;
+  __shared__ float lds[attn_merge_floats<NW, DH>() > 0 ? attn_merge_floats<NW, DH>() : 1];
+  const AttnWork w(a);
+  const int lane = w.lane, hf = w.hf;
+  const T* q = static_cast<const T*>(a.q);
+  const T* kc = static_cast<const T*>(a.kc) + ((size_t)w.b * a.H + w.h) * a.seq_pad * DH;
+  const T* vt = static_cast<const T*>(a.vt) + ((size_t)w.b * a.H + w.h) * DH * a.seq_pad;
+
+  Frag16 qf[NQF];
+#pragma unroll
+  for (int c = 0; c < NQF; ++c) {
+    const T* src = q + (size_t)w.m * a.d + w.h * DH + c * KF;
+    if constexpr (sizeof(T) == 2) {
+      qf[c] = *reinterpret_cast<const Frag16*>(src + 8 * hf);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qf[c][e] = __float_as_uint(reinterpret_cast<const float*>(src)[2 * e + hf]);
+    }
+  }
+  float mrun = -INFINITY, lrun = 0.f;
+  f32x16 o[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
+
+  for (int t = w.t0 + w.wave; t < w.t1; t += NW) {
+    const int kb = t * 32;
+    const T* krow = kc + (size_t)(kb + (lane & 31)) * DH;
+    if constexpr (sizeof(T) == 2) {
+      // the tile's K and V^T fragments are requested together (vt_col order:
+      // fragment (i, c) is 16 contiguous bytes)
+      Frag16 kf[NQF], vf[ND][2];
+#pragma unroll
+      for (int c = 0; c < NQF; ++c) kf[c] = *reinterpret_cast<const Frag16*>(krow + c * KF + 8 * hf);
+#pragma unroll
+      for (int i = 0; i < ND; ++i)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          vf[i][c] = *reinterpret_cast<const Frag16*>(vt + (size_t)(i * 32 + (lane & 31)) * a.seq_pad + kb +
+                                                      (2 * c + hf) * 8);
+      attn_tile16<T, DH>(qf, kf, vf, kb, w.limit, a.scale_log2, mrun, lrun, o, lane);
+    } else {
+      const float* kr = reinterpret_cast<const float*>(krow);
+      f32x16 s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NQF; ++c) {
+        Frag16 kf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kf[e] = __float_as_uint(kr[c * KF + 2 * e + hf]);
+        s = Mfma32<T>::mma(kf, qf[c], s);
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb + acc32_row(r, lane);
+        s[r] = key < w.limit ? s[r] * a.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, s[r]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(mrun, mx);
+      const float msafe = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = exp2f(mrun - msafe);
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = exp2f(s[r] - msafe);
+        psum += s[r];
+      }
+      psum += __shfl_xor(psum, 32);
+      lrun = lrun * alpha + psum;
+      mrun = mnew;
+#pragma unroll
+      for (int i = 0; i < ND; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+        const float* vrow = reinterpret_cast<const float*>(vt) + (size_t)(i * 32 + (lane & 31)) * a.seq_pad + kb + 4 * hf;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const Frag16 vf = *reinterpret_cast<const Frag16*>(vrow + 8 * u);
+          Frag16 pf;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pf[e] = __float_as_uint(s[4 * u + e]);
+          o[i] = Mfma32<T>::mma(vf, pf, o[i]);
+        }
+      }
+    }
+  }
+  attn_finish<T, DH, NW>(a, w, mrun, lrun, o, lds);
 }
 
 // Combine the key shares of a split attention launch in share order (one

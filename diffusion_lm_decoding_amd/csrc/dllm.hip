@@ -383,6 +383,7 @@ dllm_status launch_attn(dllm_ctx* c, int layer, const Fwd& f) {
   a.qblocks = cdiv(f.nr, 32);
   const int nwg = f.batch * m.n_heads * a.qblocks;
   const int ntile = cdiv(f.N, 32);
+  // key shares until the grid covers the 256 CUs, keeping >= 3 tiles a share
   int splits = 1;
   while (nwg * splits < 256 && ntile / (splits * 2) >= 3 && splits < kMaxAttnSplits) splits *= 2;
   const size_t rec = (size_t)(DH / 32 * 16 + 2) * 64;

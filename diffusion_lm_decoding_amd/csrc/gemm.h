@@ -27,6 +27,22 @@ struct RowGeom {
 // rows n = 16*nt + 4*(l/16) + r (r = 0..3) of token m = 16*mt + l%16.
 // ---------------------------------------------------------------------------
 
+// Column of canvas position pos in a V^T cache row.  16-bit caches store the
+// keys of each 32-key tile in the order the attention P V product consumes
+// them: slot 8 g + e (g = 2 c + h) holds key 16 c + 4 h + e for e < 4 and
+// key 16 c + 4 h + e + 4 for e >= 4, so each (key half c, lane half h)
+// fragment is 16 contiguous bytes.  fp32 caches keep natural order.
+template <typename T>
+__host__ __device__ __forceinline__ int vt_col(int pos) {
+  if constexpr (sizeof(T) == 2) {
+    const int k = pos & 31, c = k >> 4, rem = k & 15;
+    const int h = (rem >> 2) & 1, e = (rem & 3) + ((rem >> 3) << 2);
+    return (pos & ~31) + ((2 * c + h) << 3) + e;
+  } else {
+    return pos;
+  }
+}
+
 // Q/K/V projection: rotary embedding on q and k (the packed weight rows of
 // each head are ordered so that dims (j, j + dh/2) are adjacent output
 // columns 2j, 2j+1), q to a row buffer, k and v into the layer's cache rows.
@@ -36,7 +52,7 @@ struct EpiQKV {
   int d, dh, H, seq_pad;
   T* q;             // [rows][d], per-head rotary pair order
   T* kc;            // [batch][H][seq_pad][dh], rotary pair order
-  T* vt;            // [batch][H][dh][seq_pad], natural order
+  T* vt;            // [batch][H][dh][seq_pad], key order vt_col
   const float* cs;  // [seq][dh/2] cos
   const float* sn;  // [seq][dh/2] sin
   __device__ void operator()(int nt, int mt, const f32x4& acc, int lane) const {
@@ -61,7 +77,7 @@ struct EpiQKV {
       for (int t = 0; t < 4; ++t) dst[t] = Elem<T>::cvt(v[t]);
     } else {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) vt[(((size_t)b * H + h) * dh + p + t) * seq_pad + pos] = Elem<T>::cvt(v[t]);
+      for (int t = 0; t < 4; ++t) vt[(((size_t)b * H + h) * dh + p + t) * seq_pad + vt_col<T>(pos)] = Elem<T>::cvt(v[t]);
     }
   }
 };
@@ -367,41 +383,34 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmArgs a, Epi ep
 #pragma unroll
     for (int i = 0; i < MT; ++i) ssq_red[wave][i][lane] = ssq_part[i];
   }
-  if constexpr (NW > 1) {
-    __shared__ float red[NW - 1][NT * MT * 4][64];
-    if (wave > 0) {
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) red[wave - 1][(j * MT + i) * 4 + r][lane] = acc[j][i][r];
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    for (int w = 0; w < NW - 1; ++w)
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[j][i][r] += red[w][(j * MT + i) * 4 + r][lane];
-  } else {
-    __syncthreads();
-  }
-  if (a.ssq) {
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      float s = 0.f;
-      for (int w = 0; w < NW; ++w) s += ssq_red[w][i][lane & 15];
-      const float rs = 1.0f / sqrtf(s * a.inv_k + a.eps);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) acc[j][i] *= rs;
-    }
-  }
+  // every wave's partial accumulators to LDS; output tile t = j*MT + i is then
+  // summed in wave order and finished by wave t % NW, so the epilogues of the
+  // tiles run in parallel
+  constexpr int TILES = NT * MT;
+  __shared__ float red[NW][TILES * 4][64];
 #pragma unroll
   for (int j = 0; j < NT; ++j)
-    for (int i = 0; i < nmt; ++i) epi(nt0 + j, mt0 + i, acc[j][i], lane);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][(j * MT + i) * 4 + r][lane] = acc[j][i][r];
+  __syncthreads();
+  for (int t = wave; t < TILES; t += NW) {
+    const int j = t / MT, i = t % MT;
+    if (i >= nmt) continue;
+    f32x4 v;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = red[0][t * 4 + r][lane];
+    for (int w = 1; w < NW; ++w)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] += red[w][t * 4 + r][lane];
+    if (a.ssq) {
+      float s2 = 0.f;
+      for (int w = 0; w < NW; ++w) s2 += ssq_red[w][i][lane & 15];
+      v *= 1.0f / sqrtf(s2 * a.inv_k + a.eps);
+    }
+    epi(nt0 + j, mt0 + i, v, lane);
+  }
 }
 
 // ---------------------------------------------------------------------------
