@@ -27,10 +27,11 @@ pinned by library reductions (transformers' LLaMA with a bidirectional mask,
 torch SDPA / rms_norm / silu), closed forms and exact invariants.
 """
 from .model import OracleModel, KVCache
-from .sampler import select_threshold, select_factor, select_topk, select_nkeep, order_by_confidence
+from .sampler import (select_threshold, select_factor, select_topk, select_nkeep, select_budget,
+                      order_by_confidence)
 from .decode import OracleDecoder, StepRecord, lm_head_reduce
 
 __all__ = [
     "OracleModel", "KVCache", "select_threshold", "select_factor", "select_topk",
-    "select_nkeep", "order_by_confidence", "OracleDecoder", "StepRecord", "lm_head_reduce",
+    "select_nkeep", "select_budget", "order_by_confidence", "OracleDecoder", "StepRecord", "lm_head_reduce",
 ]

@@ -34,8 +34,14 @@ output).
 Parity: pinned by exact invariants (DualCache/PrefixCache with a refresh
 before every step equal uncached decoding; the first step after a refresh is
 exact), schedule closed forms (fixed-1 and tau=1 take L steps, fixed-k takes
-L/k, a dominant planted bias finishes each block in one step) and the
+L/k, a dominant planted bias finishes each block in one step, LLaDA's
+fixed-steps schedule commits floor(masked / (steps - k)) at step k) and the
 LM-head closed form with a zero head.
+
+Rules: "threshold", "factor", "topk" (k per step), "budget" (eq. (9)) and
+"steps" (LLaDA's fixed-steps schedule with k = steps per block; with
+block_len = gen_len and cache "none" it is the unblocked sampler of the
+decoding-and-speed page).
 """
 from __future__ import annotations
 
@@ -45,7 +51,7 @@ from typing import List, Optional, Tuple
 import numpy as np
 
 from .model import KVCache, OracleModel
-from .sampler import select_factor, select_threshold, select_topk
+from .sampler import select_budget, select_factor, select_nkeep, select_threshold, select_topk
 
 
 def lm_head_reduce(logits: np.ndarray, mask_id: int, target: Optional[np.ndarray] = None,
@@ -97,8 +103,10 @@ class OracleDecoder:
             raise ValueError("gen_len must be a multiple of block_len")
         if cache not in ("none", "prefix", "dual", "block_causal"):
             raise ValueError(cache)
-        if rule not in ("threshold", "factor", "topk"):
+        if rule not in ("threshold", "factor", "topk", "budget", "steps"):
             raise ValueError(rule)
+        if rule in ("topk", "steps") and k < 1:
+            raise ValueError("k must be >= 1")
         self.m = model
         self.P, self.L, self.B = prompt_len, gen_len, block_len
         self.N = prompt_len + gen_len
@@ -169,20 +177,25 @@ class OracleDecoder:
         y, c, l = lm_head_reduce(self.m.logits(h), m.mask_id, st.target[gi], st.alpha[gi])
         return cand, y, c, l
 
-    def choose(self, cand: np.ndarray, c: np.ndarray) -> np.ndarray:
+    def choose(self, cand: np.ndarray, c: np.ndarray, k_in_block: int = 0) -> np.ndarray:
+        """k_in_block: steps already taken in this block (the "steps" rule's k)."""
         if self.rule == "threshold":
             return select_threshold(c, cand, self.tau)
         if self.rule == "factor":
             return select_factor(c, cand, self.factor)
+        if self.rule == "budget":
+            return select_budget(c, cand)
+        if self.rule == "steps":
+            return select_nkeep(c, cand, self.k, k_in_block)
         return select_topk(c, cand, self.k)
 
     def step(self, st: SeqState, j: int) -> StepRecord:
+        k_in_block = sum(1 for r in st.records if r.block == j)
         cand, y, c, l = self.evaluate(st, j)
-        sel = self.choose(cand, c)
+        sel = self.choose(cand, c, k_in_block)
         idx = np.searchsorted(cand, sel)
         st.canvas[sel] = y[idx]                       # simultaneous commit
-        rec = StepRecord(j, sum(1 for r in st.records if r.block == j), cand, c, y, sel,
-                         l if self.keep_logits else None)
+        rec = StepRecord(j, k_in_block, cand, c, y, sel, l if self.keep_logits else None)
         st.records.append(rec)
         st.steps += 1
         return rec

@@ -14,7 +14,14 @@ confidences c_i = max_v p_i(v).  Comparisons are evaluated in float32.
     does": low-confidence remasking keeps the most confident predictions
     (Kim et al.'s fixed 4 tokens per step).
   * n_keep schedule of LLaDA's sampler (same section): with `steps` total
-    steps, step k keeps len(masked) // (steps - k) positions.
+    steps, step k keeps len(masked) // (steps - k) positions (possibly
+    none; the last step keeps every remaining one).
+  * non-uniform error budget: reading notes sec. 5.1, eq. (9): with
+    eps_j = 1 - c_(j) over the candidates in confidence order, keep the
+    largest n with sum_{j<=n} eps_j + max_{j<=n} eps_j < 1.  In that order
+    max_{j<=n} eps_j = eps_n.  Evaluated in float32 (eps_j = 1 - c_(j)
+    rounded, the sum accumulated in order); if no n qualifies keep the top
+    one, as the factor rule does.
 
 Ties in confidence are broken by lower position (the pages are silent).
 Pins: brute-force enumeration over small inputs (tests/test_oracle_sampler.py).
@@ -63,6 +70,24 @@ def select_topk(conf: np.ndarray, pos: np.ndarray, k: int) -> np.ndarray:
     pos = np.asarray(pos)
     order = order_by_confidence(c, pos)
     return np.sort(pos[order[:min(k, c.size)]])
+
+
+def select_budget(conf: np.ndarray, pos: np.ndarray) -> np.ndarray:
+    c = np.asarray(conf, dtype=np.float32)
+    pos = np.asarray(pos)
+    if c.size == 0:
+        return pos[:0]
+    order = order_by_confidence(c, pos)
+    best = 0
+    total = np.float32(0.0)
+    for n in range(1, c.size + 1):
+        eps_n = np.float32(np.float32(1.0) - c[order[n - 1]])
+        total = np.float32(total + eps_n)
+        if np.float32(total + eps_n) < np.float32(1.0):
+            best = n
+    if best == 0:
+        best = 1
+    return np.sort(pos[order[:best]])
 
 
 def select_nkeep(conf: np.ndarray, pos: np.ndarray, steps: int, k: int) -> np.ndarray:

@@ -61,6 +61,41 @@ def test_fixed_k_step_counts(tiny_model, k, expect):
     assert (st.canvas != TINY.mask_id).all()
 
 
+def test_unblocked_fixed_steps_sampler(tiny_model):
+    # LLaDA's sampler (decoding page): one block over the whole answer, every
+    # step a full forward, step k commits floor(masked / (steps - k))
+    pr, t, a = _inputs()
+    steps = 10
+    dec = OracleDecoder(tiny_model, 32, 64, 64, cache="none", rule="steps", k=steps)
+    st = dec.decode(pr[0], t[0], a[0])
+    assert st.steps == steps and st.refreshes == 0
+    masked = 64
+    for k, r in enumerate(st.records):
+        assert r.step == k and len(r.selected) == masked // (steps - k)
+        masked -= len(r.selected)
+    assert masked == 0 and (st.canvas != TINY.mask_id).all()
+
+
+def test_fixed_steps_per_block(tiny_model):
+    # semi-autoregressive use: the schedule restarts in every block
+    pr, t, a = _inputs()
+    dec = OracleDecoder(tiny_model, 32, 64, 16, cache="dual", rule="steps", k=5)
+    st = dec.decode(pr[0], t[0], a[0])
+    assert st.steps == 4 * 5
+    assert [len(r.selected) for r in st.records[:5]] == [3, 3, 3, 3, 4]
+
+
+def test_budget_rule_decodes(tiny_model):
+    pr, t, a = _inputs(alpha_max=16.0)
+    dec = OracleDecoder(tiny_model, 32, 64, 16, cache="dual", rule="budget")
+    st = dec.decode(pr[0], t[0], a[0])
+    assert (st.canvas != TINY.mask_id).all()
+    for r in st.records:
+        c = np.sort(r.conf[np.isin(r.cand, r.selected)].astype(np.float32))[::-1]
+        eps = 1.0 - c.astype(np.float64)
+        assert len(r.selected) == 1 or eps.sum() + eps.max() < 1.0 + 1e-6
+
+
 def test_tau_one_takes_L_steps(tiny_model):
     pr, t, a = _inputs(alpha_max=8.0)
     dec = OracleDecoder(tiny_model, 32, 64, 16, cache="dual", rule="threshold", tau=1.0)
