@@ -16,10 +16,10 @@ OK, ERR_ARG, ERR_OOM, ERR_DEVICE, ERR_STATE, ERR_NUMERIC = range(6)
 STATUS_NAMES = {0: "OK", 1: "ERR_ARG", 2: "ERR_OOM", 3: "ERR_DEVICE", 4: "ERR_STATE", 5: "ERR_NUMERIC"}
 F32, BF16 = 0, 1
 CACHE = {"none": 0, "prefix": 1, "dual": 2, "block_causal": 3}
-RULE = {"threshold": 0, "factor": 1, "topk": 2}
+RULE = {"threshold": 0, "factor": 1, "topk": 2, "budget": 3, "steps": 4}
 
-SYMBOLS = ("dllm_init_weights", "dllm_refresh_cache", "dllm_block_step", "dllm_decode",
-           "dllm_set_timing", "dllm_get_timing", "dllm_destroy", "dllm_last_error")
+SYMBOLS = ("dllm_init_weights", "dllm_refresh_cache", "dllm_block_step", "dllm_begin_decode",
+           "dllm_decode", "dllm_set_timing", "dllm_get_timing", "dllm_destroy", "dllm_last_error")
 KERNEL_CLASSES = ("embed", "rmsnorm", "qkv", "attn", "oproj", "gateup", "down", "lmhead", "merge",
                   "select")
 
@@ -114,6 +114,10 @@ def dllm_block_step(ctx: int, canvas: Canvas, cfg: DecodeCfg, block_idx: int, n_
     check(load().dllm_block_step(C.c_void_p(ctx), C.byref(canvas), C.byref(cfg), block_idx,
                                  n_committed, block_done, C.c_void_p(dbg_logits),
                                  C.c_void_p(dbg_conf), C.c_void_p(dbg_tok)))
+
+
+def dllm_begin_decode(ctx: int, canvas: Canvas, cfg: DecodeCfg) -> None:
+    check(load().dllm_begin_decode(C.c_void_p(ctx), C.byref(canvas), C.byref(cfg)))
 
 
 def dllm_decode(ctx: int, canvas: Canvas, cfg: DecodeCfg) -> Stats:

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
+#include <algorithm>
 #include <chrono>
 #include <cmath>
 #include <cstdio>
@@ -101,6 +102,8 @@ struct dllm_ctx {
   int* d_ncommit = nullptr;   // d_stat
   int* d_done = nullptr;      // d_stat + max_batch
   int* d_step = nullptr;
+  int* d_blk_id = nullptr;    // [max_batch] block of each sequence's last step
+  int* d_blk_steps = nullptr; // [max_batch] steps taken on that block
   int* h_pin = nullptr;       // pinned copy of the status block
 
   // kernel timing (dllm_set_timing): event pairs pending until the next read
@@ -229,10 +232,10 @@ dllm_status validate_decode(const dllm_ctx* ctx, const dllm_decode_cfg* d) {
   if (d->block_len > kMaxBlock) return fail(DLLM_ERR_ARG, "block_len must be <= 256");
   if (d->prompt_len + d->gen_len > ctx->cfg.max_seq) return fail(DLLM_ERR_ARG, "prompt_len + gen_len exceeds max_seq");
   if (d->cache < DLLM_CACHE_NONE || d->cache > DLLM_CACHE_BLOCK_CAUSAL) return fail(DLLM_ERR_ARG, "unknown cache mode");
-  if (d->rule < DLLM_RULE_THRESHOLD || d->rule > DLLM_RULE_TOPK) return fail(DLLM_ERR_ARG, "unknown rule");
+  if (d->rule < DLLM_RULE_THRESHOLD || d->rule > DLLM_RULE_STEPS) return fail(DLLM_ERR_ARG, "unknown rule");
   if (d->rule == DLLM_RULE_THRESHOLD && !(d->tau > 0.f && d->tau <= 1.f)) return fail(DLLM_ERR_ARG, "tau must be in (0, 1]");
   if (d->rule == DLLM_RULE_FACTOR && !(d->factor > 0.f)) return fail(DLLM_ERR_ARG, "factor must be > 0");
-  if (d->rule == DLLM_RULE_TOPK && d->k < 1) return fail(DLLM_ERR_ARG, "k must be >= 1");
+  if ((d->rule == DLLM_RULE_TOPK || d->rule == DLLM_RULE_STEPS) && d->k < 1) return fail(DLLM_ERR_ARG, "k must be >= 1");
   if (d->refresh_every < 0) return fail(DLLM_ERR_ARG, "refresh_every must be >= 0");
   return DLLM_OK;
 }
@@ -534,6 +537,9 @@ dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, in
   sa.factor = d->factor;
   sa.k = d->k;
   sa.step_ctr = c->d_step;
+  sa.block_idx = j;
+  sa.blk_id = c->d_blk_id;
+  sa.blk_steps = c->d_blk_steps;
   sa.commit_step = cv->commit_step;
   sa.ncommit = c->d_ncommit;
   sa.done = c->d_done;
@@ -650,6 +656,10 @@ dllm_status init_impl(dllm_ctx* c, const void* const* t) {
   c->d_done = c->d_stat + m.max_batch;
   c->d_err = c->d_stat + 2 * m.max_batch;
   TRY(c->alloc(&c->d_step, (size_t)m.max_batch * sizeof(int)));
+  TRY(c->alloc(&c->d_blk_id, (size_t)m.max_batch * sizeof(int)));
+  TRY(c->alloc(&c->d_blk_steps, (size_t)m.max_batch * sizeof(int)));
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, c->stream, c->d_blk_id, m.max_batch, -1);
+  TRY(check_launch());
   HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&c->h_pin), (2 * m.max_batch + 4) * sizeof(int), hipHostMallocDefault));
   HIPCHK(hipStreamSynchronize(c->stream));
   return DLLM_OK;
@@ -738,11 +748,10 @@ dllm_status dllm_block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decod
                    : step_impl<float>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok);
 }
 
-dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg* cfg, dllm_stats* stats) {
+dllm_status dllm_begin_decode(dllm_ctx* ctx, const dllm_canvas* canvas, const dllm_decode_cfg* cfg) {
   g_err.clear();
   if (!ctx || !canvas || !canvas->tokens) return fail(DLLM_ERR_ARG, "ctx, canvas and canvas->tokens must be non-NULL");
   TRY(validate_decode(ctx, cfg));
-  const auto t_start = std::chrono::steady_clock::now();
   const dllm_model_cfg& m = ctx->cfg;
   const int seq = cfg->prompt_len + cfg->gen_len;
   const int n = cfg->batch * seq;
@@ -752,18 +761,29 @@ dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cf
                      cfg->prompt_len, m.mask_id, m.vocab, ctx->d_err + 1);
   TRY(check_launch());
   HIPCHK(hipMemsetAsync(ctx->d_step, 0, cfg->batch * sizeof(int), ctx->stream));
+  HIPCHK(hipMemsetAsync(ctx->d_blk_steps, 0, cfg->batch * sizeof(int), ctx->stream));
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, ctx->stream, ctx->d_blk_id, cfg->batch, -1);
+  TRY(check_launch());
   HIPCHK(hipMemcpyAsync(ctx->h_pin + 2 * m.max_batch + 1, ctx->d_err + 1, sizeof(int), hipMemcpyDeviceToHost, ctx->stream));
   HIPCHK(hipStreamSynchronize(ctx->stream));
   if (ctx->h_pin[2 * m.max_batch + 1])
     return fail(DLLM_ERR_ARG, "canvas must hold prompt tokens (no mask_id, in vocab) followed by gen_len mask_id");
+  return DLLM_OK;
+}
+
+dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg* cfg, dllm_stats* stats) {
+  const auto t_start = std::chrono::steady_clock::now();
+  TRY(dllm_begin_decode(ctx, canvas, cfg));
 
   hipEvent_t e0, e1;
   HIPCHK(hipEventCreate(&e0));
   HIPCHK(hipEventCreate(&e1));
   double ms_refresh = 0.0;
   int64_t steps = 0, refreshes = 0, committed = 0;
-  std::vector<int> nc(cfg->batch), done(cfg->batch);
+  std::vector<int> nc(cfg->batch), done(cfg->batch), was_done(cfg->batch);
   std::vector<int64_t> seq_steps(cfg->batch, 0);
+  const bool steps_rule = cfg->rule == DLLM_RULE_STEPS;
+  const int max_in_block = steps_rule ? cfg->k : cfg->block_len;
   auto timed_refresh = [&](int blk) -> dllm_status {
     HIPCHK(hipEventRecord(e0, ctx->stream));
     TRY(dllm_refresh_cache(ctx, canvas, cfg, blk));
@@ -783,6 +803,7 @@ dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cf
   for (int j = 0; st == DLLM_OK && j < nb; ++j) {
     if (cached) st = timed_refresh(0);
     int in_block = 0;
+    std::fill(was_done.begin(), was_done.end(), 0);
     while (st == DLLM_OK) {
       if (cached && cfg->refresh_every > 0 && in_block > 0 && in_block % cfg->refresh_every == 0) {
         st = timed_refresh(0);
@@ -795,15 +816,17 @@ dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cf
       bool all_done = true, stalled = false;
       for (int b = 0; b < cfg->batch; ++b) {
         committed += nc[b];
-        if (nc[b] > 0) ++seq_steps[b];
+        if (!was_done[b]) ++seq_steps[b];
+        was_done[b] = done[b];
         if (!done[b]) {
           all_done = false;
-          if (nc[b] == 0) stalled = true;
+          if (nc[b] == 0 && !steps_rule) stalled = true;
         }
       }
       if (all_done) break;
-      if (stalled || in_block > cfg->block_len) {
-        st = fail(DLLM_ERR_STATE, "a step committed no token while masks remained");
+      if (stalled || in_block >= max_in_block) {
+        st = fail(DLLM_ERR_STATE, stalled ? "a step committed no token while masks remained"
+                                          : "a block still holds masks after its step bound");
         break;
       }
     }

@@ -125,6 +125,9 @@ struct SelectArgs {
   float tau, factor;
   int k;
   int* step_ctr;        // [batch] steps taken by each sequence
+  int block_idx;        // block of this step
+  int* blk_id;          // [batch] block of each sequence's last step (-1: none)
+  int* blk_steps;       // [batch] steps taken on that block
   int* commit_step;     // [batch][gen_len] or null
   int* ncommit;         // [batch]
   int* done;            // [batch]
@@ -136,7 +139,9 @@ struct SelectArgs {
 __global__ __launch_bounds__(256) void select_commit_kernel(SelectArgs a) {
   __shared__ float sc[256];
   __shared__ int sm[256];
+  __shared__ float eps_by_rank[256];
   __shared__ float red[4];
+  __shared__ int nbudget;
   const int b = blockIdx.x, i = threadIdx.x;
   const bool in = i < a.blk;
   int* row = a.tokens + (size_t)b * a.seq_len + a.start;
@@ -151,6 +156,7 @@ __global__ __launch_bounds__(256) void select_commit_kernel(SelectArgs a) {
   for (int j = 0; j < a.blk; ++j)
     rank += (sm[j] && (sc[j] > c || (sc[j] == c && j < i))) ? 1 : 0;
   const int n_masked = (int)block_sum<256>(masked ? 1.f : 0.f, red);
+  const int s_blk = a.blk_id[b] == a.block_idx ? a.blk_steps[b] : 0;  // steps already taken on this block
   bool sel = false;
   if (a.rule == 0) {
     sel = masked && c >= a.tau;
@@ -171,6 +177,27 @@ __global__ __launch_bounds__(256) void select_commit_kernel(SelectArgs a) {
     __syncthreads();
     if (nstar == 0) nstar = 1;
     sel = masked && rank < nstar;
+  } else if (a.rule == 3) {
+    // eq. 9 in confidence order: the float32 running sum of eps_j in that
+    // order, plus eps_n, must stay below 1; one thread walks the ranks
+    if (masked) eps_by_rank[rank] = __fsub_rn(1.0f, c);
+    __syncthreads();
+    if (i == 0) {
+      float sum = 0.f;
+      int best = 0;
+      for (int n = 1; n <= n_masked; ++n) {
+        const float e = eps_by_rank[n - 1];
+        sum = __fadd_rn(sum, e);
+        if (__fadd_rn(sum, e) < 1.0f) best = n;
+      }
+      nbudget = best > 0 ? best : 1;
+    }
+    __syncthreads();
+    sel = masked && rank < nbudget;
+  } else if (a.rule == 4) {
+    const int left = a.k - s_blk;
+    const int n_keep = left > 0 ? n_masked / left : n_masked;
+    sel = masked && rank < n_keep;
   } else {
     sel = masked && rank < a.k;
   }
@@ -184,7 +211,11 @@ __global__ __launch_bounds__(256) void select_commit_kernel(SelectArgs a) {
   if (i == 0) {
     a.ncommit[b] = cnt;
     a.done[b] = (n_masked - cnt == 0) ? 1 : 0;
-    if (n_masked > 0 && !*a.err) a.step_ctr[b] = step + 1;
+    if (n_masked > 0 && !*a.err) {
+      a.step_ctr[b] = step + 1;
+      a.blk_id[b] = a.block_idx;
+      a.blk_steps[b] = s_blk + 1;
+    }
   }
 }
 

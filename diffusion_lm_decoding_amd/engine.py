@@ -88,6 +88,11 @@ class Engine:
     def decode(self, cv: CanvasState, cfg: L.DecodeCfg) -> L.Stats:
         return L.dllm_decode(self.ctx, cv.c_struct(), cfg)
 
+    def begin(self, cv: CanvasState, cfg: L.DecodeCfg) -> None:
+        """Check the canvas and reset the step counters before driving
+        refresh/step by hand."""
+        L.dllm_begin_decode(self.ctx, cv.c_struct(), cfg)
+
     def refresh(self, cv: CanvasState, cfg: L.DecodeCfg, block_idx: int = 0) -> None:
         L.dllm_refresh_cache(self.ctx, cv.c_struct(), cfg, block_idx)
 

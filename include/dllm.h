@@ -78,9 +78,26 @@ typedef enum {
  *   FACTOR     commit the top n for the largest n with
  *              (n+1)(1 - c_(n)) < factor; if none, the top one ([RN] eq. 13,
  *              Alg. 3);
- *   TOPK       commit the top min(k, #masked) ([DS] "what one step does").
+ *   TOPK       commit the top min(k, #masked) ([DS] "what one step does");
+ *   BUDGET     with eps_j = 1 - c_(j), commit the top n for the largest n with
+ *              eps_1 + ... + eps_n + eps_n < 1 (the sum accumulated in that
+ *              order); if none, the top one ([RN] sec. 5.1, eq. 9: in
+ *              confidence order eps_n is the largest of the n);
+ *   STEPS      LLaDA's fixed-steps schedule with k steps per block: the
+ *              block's s-th step (s = 0 .. k-1, counted since
+ *              dllm_begin_decode or the last step on another block) commits
+ *              the top floor(#masked / (k - s)), possibly none; the k-th
+ *              commits the rest ([DS] the sample() listing).  With
+ *              block_len = gen_len and CACHE_NONE this is LLaDA's unblocked
+ *              sampler.
  * Comparisons are evaluated in float32. */
-typedef enum { DLLM_RULE_THRESHOLD = 0, DLLM_RULE_FACTOR = 1, DLLM_RULE_TOPK = 2 } dllm_rule;
+typedef enum {
+  DLLM_RULE_THRESHOLD = 0,
+  DLLM_RULE_FACTOR = 1,
+  DLLM_RULE_TOPK = 2,
+  DLLM_RULE_BUDGET = 3,
+  DLLM_RULE_STEPS = 4
+} dllm_rule;
 
 /* Model shape.  The architecture is pre-norm RMSNorm, rotary position
  * embedding (rotate-half pairing, absolute canvas positions), multi-head
@@ -108,7 +125,8 @@ typedef struct {
 
 /* One decode problem ([RN] Algorithm 1 inputs: prompt, answer length L,
  * block size B, selection rule).  gen_len must be a multiple of block_len;
- * tau in (0, 1]; factor > 0; k >= 1.  refresh_every > 0 additionally
+ * tau in (0, 1]; factor > 0; k >= 1 (TOPK: tokens per step; STEPS: steps
+ * per block).  refresh_every > 0 additionally
  * refreshes the cache every refresh_every steps inside a block (PREFIX/DUAL
  * only; [RN] sec. 11 decouples the refresh interval from the block size);
  * 0 refreshes only at block boundaries. */
@@ -186,7 +204,8 @@ dllm_status dllm_refresh_cache(dllm_ctx* ctx, const dllm_canvas* canvas,
  * get y_i = argmax (lowest id on ties; mask_id excluded) and
  * c_i = max softmax probability; the rule selects positions; selected
  * positions receive y_i simultaneously ([RN] Algorithm 2 step 5).  A sequence
- * whose block holds no mask commits nothing.
+ * whose block holds no mask commits nothing.  Every rule but STEPS commits at
+ * least one token of a block that holds a mask.
  *   n_committed, block_done: host int32 [batch] outputs (tokens committed by
  *     this step; 1 if the block holds no mask afterwards), or NULL.
  *   dbg_logits: device float [batch * block_len, vocab] or NULL: biased
@@ -200,14 +219,21 @@ dllm_status dllm_block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decod
                             int32_t block_idx, int32_t* n_committed, int32_t* block_done,
                             float* dbg_logits, float* dbg_conf, int32_t* dbg_tok);
 
+/* Start of a decode driven by the caller with dllm_refresh_cache /
+ * dllm_block_step: checks that the prompt holds no mask_id (and lies in
+ * [0, vocab)) and the answer region is all mask_id, and resets the
+ * per-sequence step counters (commit_step numbering, the STEPS schedule).
+ * dllm_decode does this itself.  Errors: DLLM_ERR_ARG, DLLM_ERR_DEVICE. */
+dllm_status dllm_begin_decode(dllm_ctx* ctx, const dllm_canvas* canvas, const dllm_decode_cfg* cfg);
+
 /* Whole decode ([RN] Algorithm 1, or block diffusion for BLOCK_CAUSAL):
- * checks that the prompt holds no mask_id and the answer region is all
- * mask_id, then for each block: refresh (PREFIX / DUAL) and steps until the
+ * dllm_begin_decode, then for each block: refresh (PREFIX / DUAL) and steps until the
  * block holds no mask in any sequence (lock-step over the batch; finished
  * sequences commit nothing).  No refresh follows the last block.
  *   stats: host output or NULL.
- * Errors: DLLM_ERR_ARG, DLLM_ERR_STATE (a step committed nothing while masks
- *   remained), DLLM_ERR_NUMERIC, DLLM_ERR_DEVICE. */
+ * Errors: DLLM_ERR_ARG, DLLM_ERR_STATE (a step of a rule other than STEPS
+ *   committed nothing while masks remained, or a block outlived its step
+ *   bound), DLLM_ERR_NUMERIC, DLLM_ERR_DEVICE. */
 dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg* cfg,
                         dllm_stats* stats);
 

@@ -219,8 +219,9 @@ class OracleDecoder:
                     self.refresh(st)
                 self.step(st, j)
                 n_in_block += 1
-                if st.steps > self.L:
-                    raise RuntimeError("step count exceeded the generation length")
+                # every rule but "steps" commits >= 1 per step; "steps" ends a block in k
+                if n_in_block > (self.k if self.rule == "steps" else self.B):
+                    raise RuntimeError("a block outlived its step bound")
             if self.cache == "block_causal":
                 self.commit_pass(st, j)
         return st

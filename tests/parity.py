@@ -62,11 +62,16 @@ def _exempt_sel(i, conf, rule, tau, factor, tol: Tol) -> bool:
         for r, j in enumerate(order):
             if abs((r + 2) * (1 - conf[j]) - factor) <= tol.near_rank * (r + 2):
                 return True
+    if rule == "budget":
+        eps = 1.0 - np.sort(conf)[::-1]
+        lhs = np.cumsum(eps) + eps
+        if np.any(np.abs(lhs - 1.0) <= tol.near_rank * (np.arange(eps.size) + 2)):
+            return True
     return False
 
 
 def compare_step(rep: Report, tol: Tol, dec: OracleDecoder, cand, y, c, l, gc, gt, gl, before, after,
-                 tag: str = "") -> None:
+                 k_in_block: int = 0, tag: str = "") -> None:
     """Compare one step: oracle (cand, y, c, l) against the GPU's confidences
     gc, tokens gt, logits gl (rows of cand; gl may be None) and the canvas
     before/after the GPU step."""
@@ -101,7 +106,7 @@ def compare_step(rep: Report, tol: Tol, dec: OracleDecoder, cand, y, c, l, gc, g
         gap = top2_gap(l)
     else:
         gap = np.zeros(len(cand))      # without logits only selections are checked strictly
-    o_sel = set(dec.choose(cand, c).tolist())
+    o_sel = set(dec.choose(cand, c, k_in_block).tolist())
     g_sel = set(np.nonzero(after != before)[0].tolist())
     rep.decisions += len(cand)
     for pos in sorted(o_sel ^ g_sel):
@@ -138,10 +143,12 @@ def replay(engine, cv, cfg, model: OracleModel, prompt, target, alpha, cache, ru
     def sync_canvas():
         st.canvas[:] = cv.tokens[seq].cpu().numpy()
 
+    engine.begin(cv, cfg)
     if cache == "block_causal":
         engine.refresh(cv, cfg, -1)
         dec.prefill(st)
     for j in range(Lg // B):
+        k_in_block = 0
         if cache in ("prefix", "dual"):
             engine.refresh(cv, cfg, 0)
             sync_canvas()
@@ -165,7 +172,8 @@ def replay(engine, cv, cfg, model: OracleModel, prompt, target, alpha, cache, ru
             rows = seq * B + (cand - s)
             gl = glog.cpu().numpy()[rows].astype(np.float64) if check_logits else None
             compare_step(rep, tol, dec, cand, y, c, l, gconf.cpu().numpy()[rows].astype(np.float64),
-                         gtok.cpu().numpy()[rows], gl, before, after)
+                         gtok.cpu().numpy()[rows], gl, before, after, k_in_block)
+            k_in_block += 1
         if cache == "block_causal":
             engine.refresh(cv, cfg, j)
             sync_canvas()

@@ -92,7 +92,7 @@ def test_benchmark_workload_block3_exact_point(big):
     rep = Report()
     compare_step(rep, Tol(fp32=False), dec, cand, y, c, l, gconf.cpu().numpy()[rows].astype(np.float64),
                  gtok.cpu().numpy()[rows], glog.cpu().numpy()[rows].astype(np.float64), before, after,
-                 "block 3 first step")
+                 tag="block 3 first step")
     _check(rep, "benchmark workload, block 3")
 
 
@@ -145,7 +145,7 @@ def test_batch16_first_step(big):
         rows = b * 32 + (cand - 128)
         compare_step(rep, Tol(fp32=False), dec, cand, y, c, l, gconf.cpu().numpy()[rows].astype(np.float64),
                      gtok.cpu().numpy()[rows], glog.cpu().numpy()[rows].astype(np.float64), before[b], after[b],
-                     f"sequence {b}")
+                     tag=f"sequence {b}")
     _check(rep, "batch 16")
 
 

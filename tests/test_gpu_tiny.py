@@ -55,7 +55,8 @@ def test_tiny_workload_full_decode_matches_oracle():
 
 @pytest.mark.parametrize("cache", ["dual", "prefix", "none", "block_causal"])
 @pytest.mark.parametrize("rule,kw", [("threshold", dict(tau=0.9)), ("factor", dict(factor=1.0)),
-                                     ("factor", dict(factor=2.0)), ("topk", dict(k=4))])
+                                     ("factor", dict(factor=2.0)), ("topk", dict(k=4)), ("budget", {}),
+                                     ("steps", dict(k=5))])
 def test_f32_lockstep(engines, cache, rule, kw):
     from diffusion_lm_decoding_amd.engine import Engine
     eng, om = engines["f32"]
@@ -68,7 +69,8 @@ def test_f32_lockstep(engines, cache, rule, kw):
 
 
 @pytest.mark.parametrize("cache", ["dual", "prefix", "none", "block_causal"])
-@pytest.mark.parametrize("rule,kw", [("threshold", dict(tau=0.9)), ("factor", dict(factor=1.0))])
+@pytest.mark.parametrize("rule,kw", [("threshold", dict(tau=0.9)), ("factor", dict(factor=1.0)),
+                                     ("budget", {})])
 def test_bf16_lockstep(engines, cache, rule, kw):
     from diffusion_lm_decoding_amd.engine import Engine
     eng, om = engines["bf16"]
@@ -135,6 +137,26 @@ def test_schedules_on_gpu(engines):
     cv = eng.canvas(pr, t, a * 0 + 8.0, 64)
     st = eng.decode(cv, Engine.decode_cfg(1, 32, 64, 16, cache="dual", tau=1.0))
     assert st.steps == 64
+
+
+@pytest.mark.parametrize("block,steps", [(64, 10), (16, 20)])
+def test_fixed_steps_sampler_full_decode(engines, block, steps):
+    """LLaDA's sampler: unblocked (one block, no cache) and with more steps
+    than block positions (steps that commit nothing): tokens, commit steps
+    and step counts identical to the oracle."""
+    from diffusion_lm_decoding_amd.engine import Engine
+    eng, om = engines["f32"]
+    pr, t, a = _inputs(1, 32, 64, seed=81, alpha_max=8.0)
+    cache = "none" if block == 64 else "dual"
+    cv = eng.canvas(pr, t, a, 64)
+    stats = eng.decode(cv, Engine.decode_cfg(1, 32, 64, block, cache=cache, rule="steps", k=steps))
+    dec = OracleDecoder(om, 32, 64, block, cache=cache, rule="steps", k=steps)
+    st = dec.decode(pr[0], t[0], a[0])
+    assert np.array_equal(cv.tokens.cpu().numpy()[0], st.canvas)
+    assert stats.steps == st.steps == steps * (64 // block)
+    cs = cv.commit_step.cpu().numpy()[0]
+    for k, rec in enumerate(st.records):
+        assert (cs[rec.selected - 32] == k).all()
 
 
 def test_bad_canvas_rejected(engines):
