@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--rule", default="", help="override the rule")
     p.add_argument("--cpu-steps", type=int, default=16, help="oracle denoising steps timed for cpu_baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-b16", action="store_true", help="skip the batch-16 projection MFMA-fraction measurement")
+    p.add_argument("--no-peaks", action="store_true", help="skip the achievable-peak microkernels")
     p.add_argument("--probe", type=int, default=0, metavar="STEPS",
                    help="counter-collection mode: one cache pass, STEPS denoising steps of block 0 and a "
                         "copy of COPY_MIB MiB (read once, written once) that calibrates the byte counters; "
@@ -93,7 +95,16 @@ def main():
             host_weights[name] = a
         return a
 
-    eng = Engine(shape, get, max_batch=w.batch, max_seq=w.seq_len, device="cuda:0")
+    peaks = None
+    if not args.no_peaks and not args.probe:
+        hbm, mfma = L.dllm_probe_peaks(8 << 30)
+        peaks = {"hbm_gbs": hbm, "mfma_f16_tflops": mfma,
+                 "how": "library microkernels: streaming read of 8 GiB; 16x16x32 fp16 MFMA chains from registers"}
+        log(f"[bench] achievable: HBM read {hbm:.0f} GB/s, fp16 MFMA {mfma:.0f} TFLOP/s")
+    b16 = None if (args.no_b16 or args.probe) else workload("llada8b_p128_g128")
+    max_batch = max(w.batch, b16.batch if b16 else 0)
+    max_seq = max(w.seq_len, b16.seq_len if b16 else 0)
+    eng = Engine(shape, get, max_batch=max_batch, max_seq=max_seq, device="cuda:0")
     log(f"[bench] weights generated and packed in {time.time() - t0:.1f} s")
     prompt = gen_prompt(shape, w.batch, w.prompt_len, w.prompt_seed)
     target, alpha = gen_bias(shape, w.batch, w.gen_len, w.bias_seed, w.alpha_max)
@@ -127,6 +138,9 @@ def main():
     committed = sum(s.committed for s in stats)
     steps = sum(s.steps for s in stats)
     refresh_ms = sum(s.ms_refresh for s in stats)
+    # every DualCache/PrefixCache refresh recomputes the whole canvas, so the
+    # first (prompt) refresh of a decode costs ms_refresh / refreshes
+    first_refresh_ms = sum(s.ms_refresh / max(s.refreshes, 1) for s in stats)
     dtype = "f16" if shape.dtype == "bf16" else "f32"
     n = max(kt["launches"], 1)
     intensity = kt["flops"] / max(kt["bytes"], 1.0)
@@ -162,8 +176,25 @@ def main():
         "tokens_per_denoise_step": committed / max(steps, 1),
         "ms_per_denoise_step": (elapsed * 1e3 - refresh_ms) / max(steps, 1),
         "ms_refresh_per_decode": refresh_ms / args.steps,
+        "value_excl_initial_refresh": committed / (elapsed - first_refresh_ms / 1e3),
         "roofline": roof,
     }
+    ms_step = (elapsed * 1e3 - refresh_ms) / max(steps, 1)
+    if shape.name == "llada8b" and w.batch == 1 and w.cache == "dual":
+        # whole denoising step against HBM: weights (layers + LM head) read once,
+        # the canvas's K/V read, the block's K/V written
+        n_params = shape.n_layers * (4 * shape.d_model ** 2 + 3 * shape.d_model * shape.d_ffn) + \
+            shape.vocab * shape.d_model
+        kv_pos = 2 * shape.n_layers * shape.d_model * 2
+        alg = 2 * n_params + kv_pos * w.seq_len + kv_pos * w.block_len
+        out["step_hbm_fraction"] = {"value": alg / (HBM_PEAK_GBS * 1e9) / (ms_step / 1e3),
+                                    "algorithmic_bytes": alg, "ms_per_step": ms_step, "peak_gbs": HBM_PEAK_GBS}
+        if peaks:
+            out["step_hbm_fraction"]["vs_achievable"] = alg / (peaks["hbm_gbs"] * 1e9) / (ms_step / 1e3)
+    if peaks:
+        out["achievable"] = peaks
+    if b16 is not None:
+        out["b16_projection_mfma_fraction"] = b16_projections(eng, b16, L)
     eng.close()
     del eng
     if not args.no_cpu_baseline:
@@ -193,6 +224,36 @@ def probe(eng, w, prompt, target, alpha, n_steps, dev):
     print(json.dumps({"probe": w.name, "denoising_steps": n_steps, "copy_bytes_read": n * 4,
                       "copy_bytes_written": n * 4}), flush=True)
     eng.close()
+
+
+def b16_projections(eng, w, L, n_steps=3):
+    """MFMA fraction of the batch-16 projection GEMMs: the projection flops of
+    one denoising step (2 x rows x layer parameters) over their summed kernel
+    time, against the dense fp16 peak.  Block 0 of the batch-16 DualCache
+    workload, one refresh then n_steps steps."""
+    from diffusion_lm_decoding_amd.engine import Engine
+    from workloads import gen_bias, gen_prompt
+    shape = w.model
+    prompt = gen_prompt(shape, w.batch, w.prompt_len, w.prompt_seed)
+    target, alpha = gen_bias(shape, w.batch, w.gen_len, w.bias_seed, w.alpha_max)
+    cfg = Engine.cfg_from_workload(w)
+    cv = eng.canvas(prompt, target, alpha, w.gen_len)
+    eng.begin(cv, cfg)
+    eng.refresh(cv, cfg, 0)
+    gemms = ["qkv", "oproj", "gateup", "down"]
+    L.dllm_get_timing(eng.ctx, reset=True)
+    L.dllm_set_timing(eng.ctx, gemms)
+    for _ in range(n_steps):
+        eng.step(cv, cfg, 0)
+    L.dllm_set_timing(eng.ctx, [])
+    kt = L.dllm_get_timing(eng.ctx, reset=True)["step"]
+    ms = sum(kt[g]["ms"] for g in gemms) / n_steps
+    rows = w.batch * w.block_len
+    flops = 2.0 * rows * shape.n_layers * (4 * shape.d_model ** 2 + 3 * shape.d_model * shape.d_ffn)
+    frac = flops / (ms / 1e3) / (PEAKS_TFLOPS["f16"] * 1e12)
+    log(f"[bench] batch-16 projections: {ms:.3f} ms per step, {flops / ms / 1e9:.0f} TFLOP/s, {100 * frac:.1f}% of peak")
+    return {"value": frac, "flops_per_step": flops, "gemm_ms_per_step": ms, "peak_tflops": PEAKS_TFLOPS["f16"],
+            "workload": w.name, "steps": n_steps}
 
 
 def stored_traffic(workload, cls):

@@ -19,7 +19,8 @@ CACHE = {"none": 0, "prefix": 1, "dual": 2, "block_causal": 3}
 RULE = {"threshold": 0, "factor": 1, "topk": 2, "budget": 3, "steps": 4}
 
 SYMBOLS = ("dllm_init_weights", "dllm_refresh_cache", "dllm_block_step", "dllm_begin_decode",
-           "dllm_decode", "dllm_set_timing", "dllm_get_timing", "dllm_destroy", "dllm_last_error")
+           "dllm_decode", "dllm_set_timing", "dllm_get_timing", "dllm_probe_peaks", "dllm_destroy",
+           "dllm_last_error")
 KERNEL_CLASSES = ("embed", "rmsnorm", "qkv", "attn", "oproj", "gateup", "down", "lmhead", "merge",
                   "select")
 
@@ -78,6 +79,10 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.dllm_block_step.argtypes = [P, C.POINTER(Canvas), C.POINTER(DecodeCfg), C.c_int32,
                                     C.POINTER(C.c_int32), C.POINTER(C.c_int32), P, P, P]
     lib.dllm_block_step.restype = C.c_int
+    lib.dllm_begin_decode.argtypes = [P, C.POINTER(Canvas), C.POINTER(DecodeCfg)]
+    lib.dllm_begin_decode.restype = C.c_int
+    lib.dllm_probe_peaks.argtypes = [C.c_uint64, C.POINTER(C.c_double), C.POINTER(C.c_double)]
+    lib.dllm_probe_peaks.restype = C.c_int
     lib.dllm_decode.argtypes = [P, C.POINTER(Canvas), C.POINTER(DecodeCfg), C.POINTER(Stats)]
     lib.dllm_decode.restype = C.c_int
     lib.dllm_set_timing.argtypes = [P, C.c_uint32]
@@ -124,6 +129,13 @@ def dllm_decode(ctx: int, canvas: Canvas, cfg: DecodeCfg) -> Stats:
     st = Stats()
     check(load().dllm_decode(C.c_void_p(ctx), C.byref(canvas), C.byref(cfg), C.byref(st)))
     return st
+
+
+def dllm_probe_peaks(nbytes: int = 8 << 30):
+    """(achievable HBM read GB/s, achievable fp16 MFMA TFLOP/s) of device 0."""
+    hbm, mfma = C.c_double(0.0), C.c_double(0.0)
+    check(load().dllm_probe_peaks(C.c_uint64(nbytes), C.byref(hbm), C.byref(mfma)))
+    return hbm.value, mfma.value
 
 
 def dllm_set_timing(ctx: int, classes) -> None:

@@ -16,6 +16,7 @@
 #include "attention.h"
 #include "gemm.h"
 #include "ops.h"
+#include "probe.h"
 
 using namespace dllm;
 
@@ -718,6 +719,68 @@ dllm_status dllm_get_timing(dllm_ctx* ctx, dllm_kernel_time* out, int32_t reset)
   if (reset)
     for (int i = 0; i < 2 * DLLM_K_COUNT; ++i) ctx->timing[i] = dllm_kernel_time{};
   return DLLM_OK;
+}
+
+dllm_status dllm_probe_peaks(uint64_t bytes, double* hbm_gbs, double* mfma_f16_tflops) {
+  g_err.clear();
+  if (bytes < (1u << 20)) return fail(DLLM_ERR_ARG, "bytes must be >= 1 MiB");
+  hipDeviceProp_t prop;
+  HIPCHK(hipGetDeviceProperties(&prop, 0));
+  hipStream_t s = nullptr;
+  HIPCHK(hipStreamCreate(&s));
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  void* buf = nullptr;
+  unsigned* sink = nullptr;
+  dllm_status st = DLLM_OK;
+  auto done = [&](dllm_status r) {
+    if (buf) (void)hipFree(buf);
+    if (sink) (void)hipFree(sink);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    (void)hipStreamDestroy(s);
+    return r;
+  };
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess)
+    return done(fail(DLLM_ERR_DEVICE, "hipEventCreate failed"));
+  if (hipMalloc(&sink, 64) != hipSuccess) return done(fail(DLLM_ERR_OOM, "hipMalloc failed"));
+  const size_t n16 = (size_t)(bytes / 16);
+  if (hbm_gbs) {
+    if (hipMalloc(&buf, n16 * 16) != hipSuccess) {
+      (void)hipGetLastError();
+      return done(fail(DLLM_ERR_OOM, "hipMalloc of the probe buffer failed"));
+    }
+    if (hipMemsetAsync(buf, 1, n16 * 16, s) != hipSuccess) return done(fail(DLLM_ERR_DEVICE, "hipMemsetAsync failed"));
+    const unsigned grid = (unsigned)prop.multiProcessorCount * 8;
+    float best = 1e30f;
+    for (int rep = 0; rep < 4; ++rep) {
+      (void)hipEventRecord(e0, s);
+      hipLaunchKernelGGL(hbm_read_kernel, dim3(grid), dim3(256), 0, s, static_cast<const Frag16*>(buf), n16, sink);
+      (void)hipEventRecord(e1, s);
+      if (hipEventSynchronize(e1) != hipSuccess) return done(fail(DLLM_ERR_DEVICE, "probe kernel failed"));
+      float ms = 0.f;
+      (void)hipEventElapsedTime(&ms, e0, e1);
+      if (rep > 0 && ms < best) best = ms;
+    }
+    *hbm_gbs = (double)n16 * 16 / (best * 1e6);
+  }
+  if (mfma_f16_tflops) {
+    const int iters = 20000;
+    const unsigned grid = (unsigned)prop.multiProcessorCount * 8;   // 8 waves per SIMD pair slot
+    float best = 1e30f;
+    for (int rep = 0; rep < 3; ++rep) {
+      (void)hipEventRecord(e0, s);
+      hipLaunchKernelGGL(mfma_loop_kernel, dim3(grid), dim3(256), 0, s, iters, reinterpret_cast<float*>(sink));
+      (void)hipEventRecord(e1, s);
+      if (hipEventSynchronize(e1) != hipSuccess) return done(fail(DLLM_ERR_DEVICE, "probe kernel failed"));
+      float ms = 0.f;
+      (void)hipEventElapsedTime(&ms, e0, e1);
+      if (rep > 0 && ms < best) best = ms;
+    }
+    const double flops = (double)grid * 4 /* waves */ * iters * 8 * (2.0 * 16 * 16 * 32);
+    *mfma_f16_tflops = flops / (best * 1e9);
+  }
+  (void)st;
+  return done(DLLM_OK);
 }
 
 void dllm_destroy(dllm_ctx* ctx) {
