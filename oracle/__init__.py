@@ -30,8 +30,10 @@ from .model import OracleModel, KVCache
 from .sampler import (select_threshold, select_factor, select_topk, select_nkeep, select_budget,
                       order_by_confidence)
 from .decode import OracleDecoder, StepRecord, lm_head_reduce
+from .diagnostics import cosine_rows, staleness
 
 __all__ = [
     "OracleModel", "KVCache", "select_threshold", "select_factor", "select_topk",
     "select_nkeep", "select_budget", "order_by_confidence", "OracleDecoder", "StepRecord", "lm_head_reduce",
+    "cosine_rows", "staleness",
 ]
