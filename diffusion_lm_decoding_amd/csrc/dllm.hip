@@ -493,16 +493,15 @@ dllm_status refresh_impl(dllm_ctx* c, const dllm_canvas* cv, const dllm_decode_c
   return forward<T>(c, f);
 }
 
+// The rows a step of cache mode `cache` recomputes, the forward over them and
+// the LM-head reduction of block j's rows into c->conf / c->tok (no commit).
 template <typename T>
-dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, int j, int* n_committed,
-                      int* block_done, float* dbg_logits, float* dbg_conf, int* dbg_tok) {
+dllm_status eval_block(dllm_ctx* c, const dllm_canvas* cv, const dllm_decode_cfg* d, int j, int cache,
+                       float* dbg_logits) {
   const dllm_model_cfg& m = c->cfg;
-  if (j < 0 || j >= d->gen_len / d->block_len) return fail(DLLM_ERR_ARG, "block_idx out of range");
-  if ((cv->bias_target == nullptr) != (cv->bias_alpha == nullptr))
-    return fail(DLLM_ERR_ARG, "bias_target and bias_alpha must both be set or both NULL");
   Fwd f = make_fwd(c, cv, d);
   const int s = d->prompt_len + j * d->block_len;
-  switch (d->cache) {
+  switch (cache) {
     case DLLM_CACHE_NONE: f.row_start = 0; f.nr = f.seq_len; break;
     case DLLM_CACHE_PREFIX: f.row_start = s; f.nr = f.seq_len - s; break;
     default: f.row_start = s; f.nr = d->block_len; break;
@@ -517,12 +516,23 @@ dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, in
   hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, c->stream, c->d_err, 2, 0);
   TRY(check_launch());
   TRY(launch_gemm<T>(c, DLLM_K_LMHEAD, c->xh, c->wlm, HR, m.vocab, m.d_model, eh, c->ssq_head, HR));
-  {
-    Timed tm(c, DLLM_K_MERGE, 12.0 * c->n_vtiles * HR + 8.0 * HR, 3.0 * c->n_vtiles * HR);
-    hipLaunchKernelGGL(lm_merge_kernel, dim3(HR), dim3(kMergeThreads), 0, c->stream, c->pmax, c->psum, c->parg, c->n_vtiles,
-                       HR, c->conf, c->tok, c->d_err);
-    TRY(tm.done());
-  }
+  Timed tm(c, DLLM_K_MERGE, 12.0 * c->n_vtiles * HR + 8.0 * HR, 3.0 * c->n_vtiles * HR);
+  hipLaunchKernelGGL(lm_merge_kernel, dim3(HR), dim3(kMergeThreads), 0, c->stream, c->pmax, c->psum, c->parg, c->n_vtiles,
+                     HR, c->conf, c->tok, c->d_err);
+  return tm.done();
+}
+
+template <typename T>
+dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, int j, int* n_committed,
+                      int* block_done, float* dbg_logits, float* dbg_conf, int* dbg_tok) {
+  const dllm_model_cfg& m = c->cfg;
+  if (j < 0 || j >= d->gen_len / d->block_len) return fail(DLLM_ERR_ARG, "block_idx out of range");
+  if ((cv->bias_target == nullptr) != (cv->bias_alpha == nullptr))
+    return fail(DLLM_ERR_ARG, "bias_target and bias_alpha must both be set or both NULL");
+  const int s = d->prompt_len + j * d->block_len;
+  const int B = d->block_len, HR = d->batch * B;
+  TRY(eval_block<T>(c, cv, d, j, d->cache, dbg_logits));
+  Fwd f = make_fwd(c, cv, d);
   SelectArgs sa{};
   sa.tokens = cv->tokens;
   sa.seq_len = f.seq_len;
@@ -560,6 +570,74 @@ dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, in
     if (n_committed) n_committed[b] = c->h_pin[b];
     if (block_done) block_done[b] = c->h_pin[mb + b];
   }
+  return DLLM_OK;
+}
+
+// Cached-vs-fresh diagnostics of block j at the current canvas (see the
+// header): snapshot the sequences' K/V, evaluate from the cache, evaluate from
+// a full fresh forward, compare the snapshot with the fresh K/V, restore.
+template <typename T>
+dllm_status staleness_impl(dllm_ctx* c, const dllm_canvas* cv, const dllm_decode_cfg* d, int j, float* conf_cached,
+                           int* tok_cached, float* conf_fresh, int* tok_fresh, float* k_cos, float* v_cos) {
+  const dllm_model_cfg& m = c->cfg;
+  if (j < 0 || j >= d->gen_len / d->block_len) return fail(DLLM_ERR_ARG, "block_idx out of range");
+  if (d->cache == DLLM_CACHE_BLOCK_CAUSAL)
+    return fail(DLLM_ERR_ARG, "the block-causal cache is exact; staleness is defined for NONE, PREFIX and DUAL");
+  if ((cv->bias_target == nullptr) != (cv->bias_alpha == nullptr))
+    return fail(DLLM_ERR_ARG, "bias_target and bias_alpha must both be set or both NULL");
+  const int L = m.n_layers, N = d->prompt_len + d->gen_len, s = d->prompt_len + j * d->block_len;
+  const size_t slice = (size_t)d->batch * m.n_heads * c->seq_pad * m.head_dim;  // elements per layer
+  const size_t es = sizeof(T);
+  T* saved = nullptr;
+  if (hipMalloc(&saved, 2 * slice * L * es) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DLLM_ERR_OOM, "hipMalloc of the K/V snapshot failed");
+  }
+  auto kc = [&](int l) { return static_cast<T*>(c->kc) + (size_t)l * c->kv_layer; };
+  auto vt = [&](int l) { return static_cast<T*>(c->vt) + (size_t)l * c->kv_layer; };
+  dllm_status st = DLLM_OK;
+  auto copy_kv = [&](bool save) -> dllm_status {
+    for (int l = 0; l < L; ++l) {
+      T* ks = saved + (2 * (size_t)l) * slice;
+      T* vs = ks + slice;
+      HIPCHK(hipMemcpyAsync(save ? ks : kc(l), save ? kc(l) : ks, slice * es, hipMemcpyDeviceToDevice, c->stream));
+      HIPCHK(hipMemcpyAsync(save ? vs : vt(l), save ? vt(l) : vs, slice * es, hipMemcpyDeviceToDevice, c->stream));
+    }
+    return DLLM_OK;
+  };
+  auto body = [&]() -> dllm_status {
+    TRY(copy_kv(true));
+    const int B = d->block_len;
+    TRY(eval_block<T>(c, cv, d, j, d->cache, nullptr));
+    hipLaunchKernelGGL(masked_copy_kernel, dim3(d->batch), dim3(256), 0, c->stream, cv->tokens, N, s, B, m.mask_id,
+                       c->conf, c->tok, conf_cached, tok_cached);
+    TRY(check_launch());
+    TRY(eval_block<T>(c, cv, d, j, DLLM_CACHE_NONE, nullptr));
+    hipLaunchKernelGGL(masked_copy_kernel, dim3(d->batch), dim3(256), 0, c->stream, cv->tokens, N, s, B, m.mask_id,
+                       c->conf, c->tok, conf_fresh, tok_fresh);
+    TRY(check_launch());
+    if (k_cos || v_cos) {
+      const int items = d->batch * N;
+      for (int l = 0; l < L; ++l) {
+        const T* ks = saved + (2 * (size_t)l) * slice;
+        hipLaunchKernelGGL((kv_cosine_kernel<T>), dim3(cdiv(items, 4)), dim3(256), 0, c->stream, ks, ks + slice,
+                           kc(l), vt(l), m.n_heads, m.head_dim, c->seq_pad, N, d->batch,
+                           k_cos ? k_cos + (size_t)l * items : nullptr, v_cos ? v_cos + (size_t)l * items : nullptr);
+        TRY(check_launch());
+      }
+    }
+    return DLLM_OK;
+  };
+  st = body();
+  const dllm_status rs = copy_kv(false);   // restore even after a failure
+  const hipError_t e = hipStreamSynchronize(c->stream);
+  (void)hipFree(saved);
+  if (st != DLLM_OK) return st;
+  if (rs != DLLM_OK) return rs;
+  if (e != hipSuccess) return fail(DLLM_ERR_DEVICE, std::string("staleness: ") + hipGetErrorString(e));
+  int err = 0;
+  HIPCHK(hipMemcpy(&err, c->d_err, sizeof(int), hipMemcpyDeviceToHost));
+  if (err) return fail(DLLM_ERR_NUMERIC, "non-finite logits or confidence in the LM head");
   return DLLM_OK;
 }
 
@@ -809,6 +887,18 @@ dllm_status dllm_block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decod
   if ((dbg_conf == nullptr) != (dbg_tok == nullptr)) return fail(DLLM_ERR_ARG, "dbg_conf and dbg_tok must both be set or both NULL");
   return ctx->bf16 ? step_impl<f16_t>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok)
                    : step_impl<float>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok);
+}
+
+dllm_status dllm_staleness(dllm_ctx* ctx, const dllm_canvas* canvas, const dllm_decode_cfg* cfg, int32_t block_idx,
+                           float* conf_cached, int32_t* tok_cached, float* conf_fresh, int32_t* tok_fresh,
+                           float* k_cos, float* v_cos) {
+  g_err.clear();
+  if (!ctx || !canvas || !canvas->tokens) return fail(DLLM_ERR_ARG, "ctx, canvas and canvas->tokens must be non-NULL");
+  TRY(validate_decode(ctx, cfg));
+  return ctx->bf16 ? staleness_impl<f16_t>(ctx, canvas, cfg, block_idx, conf_cached, tok_cached, conf_fresh, tok_fresh,
+                                           k_cos, v_cos)
+                   : staleness_impl<float>(ctx, canvas, cfg, block_idx, conf_cached, tok_cached, conf_fresh, tok_fresh,
+                                           k_cos, v_cos);
 }
 
 dllm_status dllm_begin_decode(dllm_ctx* ctx, const dllm_canvas* canvas, const dllm_decode_cfg* cfg) {

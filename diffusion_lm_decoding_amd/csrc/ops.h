@@ -219,6 +219,52 @@ __global__ __launch_bounds__(256) void select_commit_kernel(SelectArgs a) {
   }
 }
 
+// ---- staleness diagnostics ---------------------------------------------------
+// out[b][i] = (conf, tok) of block row i of sequence b if that row is still
+// MASK, else (-1, -1).
+__global__ __launch_bounds__(256) void masked_copy_kernel(const int* tokens, int seq_len, int start, int blk,
+                                                          int mask_id, const float* conf, const int* tok,
+                                                          float* out_conf, int* out_tok) {
+  const int b = blockIdx.x, i = threadIdx.x;
+  if (i >= blk) return;
+  const bool masked = tokens[(size_t)b * seq_len + start + i] == mask_id;
+  if (out_conf) out_conf[b * blk + i] = masked ? conf[b * blk + i] : -1.0f;
+  if (out_tok) out_tok[b * blk + i] = masked ? tok[b * blk + i] : -1;
+}
+
+// Cosine similarity, per (sequence, canvas position), between two copies of
+// one layer's K (and V) over all heads: <a, b> / (|a| |b|), 1 when both are
+// zero, 0 when one is.  One wave per position; K [batch][H][seq_pad][dh], V^T
+// [batch][H][dh][seq_pad] in vt_col order.
+template <typename T>
+__global__ __launch_bounds__(256) void kv_cosine_kernel(const T* k_a, const T* v_a, const T* k_b, const T* v_b,
+                                                        int H, int dh, int seq_pad, int N, int batch,
+                                                        float* k_cos, float* v_cos) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= batch * N) return;
+  const int b = item / N, pos = item % N;
+  float kd = 0.f, ka = 0.f, kb = 0.f, vd = 0.f, va = 0.f, vb = 0.f;
+  for (int e = lane; e < H * dh; e += 64) {
+    const int h = e / dh, d = e % dh;
+    const size_t ko = (((size_t)b * H + h) * seq_pad + pos) * dh + d;
+    const size_t vo = (((size_t)b * H + h) * dh + d) * seq_pad + vt_col<T>(pos);
+    const float x = Elem<T>::load(k_a + ko), y = Elem<T>::load(k_b + ko);
+    const float u = Elem<T>::load(v_a + vo), w = Elem<T>::load(v_b + vo);
+    kd += x * y; ka += x * x; kb += y * y;
+    vd += u * w; va += u * u; vb += w * w;
+  }
+  kd = wave_sum(kd); ka = wave_sum(ka); kb = wave_sum(kb);
+  vd = wave_sum(vd); va = wave_sum(va); vb = wave_sum(vb);
+  if (lane != 0) return;
+  auto cosv = [](float d, float a, float bb) {
+    if (a == 0.f || bb == 0.f) return (a == 0.f && bb == 0.f) ? 1.f : 0.f;
+    return d / sqrtf(a * bb);
+  };
+  if (k_cos) k_cos[item] = cosv(kd, ka, kb);
+  if (v_cos) v_cos[item] = cosv(vd, va, vb);
+}
+
 // ---- canvas check: prompt holds no mask, answer region is all mask ---------
 __global__ __launch_bounds__(256) void canvas_check_kernel(const int* tokens, int n, int seq_len,
                                                            int prompt_len, int mask_id, int vocab,

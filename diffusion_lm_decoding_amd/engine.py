@@ -115,6 +115,22 @@ class Engine:
                           tok.data_ptr() if tok is not None else 0)
         return np.array(nc[:]), np.array(dn[:]), conf, tok, logits
 
+    def staleness(self, cv: CanvasState, cfg: L.DecodeCfg, block_idx: int) -> dict:
+        """Cached-vs-fresh evaluation of block block_idx at the current canvas
+        and the per-layer, per-position K/V cosine of the cache against a fresh
+        forward (device tensors); the cache is left unchanged."""
+        b, B, N = cfg.batch, cfg.block_len, cfg.prompt_len + cfg.gen_len
+        dev = self.device
+        out = {"conf_cached": torch.empty(b * B, dtype=torch.float32, device=dev),
+               "tok_cached": torch.empty(b * B, dtype=torch.int32, device=dev),
+               "conf_fresh": torch.empty(b * B, dtype=torch.float32, device=dev),
+               "tok_fresh": torch.empty(b * B, dtype=torch.int32, device=dev),
+               "k_cos": torch.empty(self.shape.n_layers, b, N, dtype=torch.float32, device=dev),
+               "v_cos": torch.empty(self.shape.n_layers, b, N, dtype=torch.float32, device=dev)}
+        L.dllm_staleness(self.ctx, cv.c_struct(), cfg, block_idx, *(out[k].data_ptr() for k in
+                         ("conf_cached", "tok_cached", "conf_fresh", "tok_fresh", "k_cos", "v_cos")))
+        return out
+
     def close(self) -> None:
         if getattr(self, "ctx", None):
             L.dllm_destroy(self.ctx)

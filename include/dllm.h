@@ -219,6 +219,30 @@ dllm_status dllm_block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decod
                             int32_t block_idx, int32_t* n_committed, int32_t* block_done,
                             float* dbg_logits, float* dbg_conf, int32_t* dbg_tok);
 
+/* Cached-vs-fresh diagnostics at the current canvas ([RN] sec. 14 and
+ * Algorithm 4 steps 4-5: compare fresh and cached predictions at the commit
+ * positions, and how far the cached K/V have drifted).  For block block_idx
+ * of every sequence it evaluates the block's rows twice without committing:
+ * as a block step of cfg->cache would, from the current (possibly stale)
+ * cache, and from a full fresh forward over the canvas (the no-cache step).
+ * It also compares, per layer and canvas position, the cached K and V (as
+ * they were on entry) with the fresh ones.  The cache is restored before the
+ * call returns, so a decode continues exactly as without it.  cfg->cache must
+ * be NONE, PREFIX or DUAL.  Allocates a temporary device snapshot of the K/V
+ * of cfg->batch sequences (2 x n_layers x batch x n_heads x max_seq x head_dim
+ * elements).
+ *   conf_cached, tok_cached, conf_fresh, tok_fresh: device float / int32
+ *     [batch * block_len] or NULL: c_i and y_i of the block's masked rows
+ *     (-1 for rows already committed).
+ *   k_cos, v_cos: device float [n_layers, batch, prompt_len + gen_len] or NULL:
+ *     <cached, fresh> / (|cached| |fresh|) over all heads of the position
+ *     (1 if both are zero, 0 if one is).
+ * Blocks until done.  Errors: DLLM_ERR_ARG, DLLM_ERR_OOM, DLLM_ERR_NUMERIC,
+ *   DLLM_ERR_DEVICE. */
+dllm_status dllm_staleness(dllm_ctx* ctx, const dllm_canvas* canvas, const dllm_decode_cfg* cfg, int32_t block_idx,
+                           float* conf_cached, int32_t* tok_cached, float* conf_fresh, int32_t* tok_fresh,
+                           float* k_cos, float* v_cos);
+
 /* Start of a decode driven by the caller with dllm_refresh_cache /
  * dllm_block_step: checks that the prompt holds no mask_id (and lies in
  * [0, vocab)) and the answer region is all mask_id, and resets the

@@ -41,12 +41,13 @@ def staleness(dec: OracleDecoder, st: SeqState, j: int) -> dict:
         raise ValueError("the block-causal cache is exact")
     m = dec.m.shape
     entry = st.kv.copy()
-    cand, y_c, c_c, _ = dec.evaluate(st, j)
+    cand, y_c, c_c, l_c = dec.evaluate(st, j)
     fresh = KVCache(m.n_layers, dec.N, m.n_heads, m.head_dim)
     rows = np.arange(dec.N)
     hidden = dec.m.forward_rows(st.canvas, rows, fresh, np.full(dec.N, dec.N))
     gi = cand - dec.P
-    y_f, c_f, _ = lm_head_reduce(dec.m.logits(hidden[cand]), m.mask_id, st.target[gi], st.alpha[gi])
+    y_f, c_f, l_f = lm_head_reduce(dec.m.logits(hidden[cand]), m.mask_id, st.target[gi], st.alpha[gi])
     st.kv = entry
     return {"cand": cand, "tok_cached": y_c, "conf_cached": c_c, "tok_fresh": y_f, "conf_fresh": c_f,
+            "logits_cached": l_c, "logits_fresh": l_f,
             "k_cos": cosine_rows(entry.k, fresh.k), "v_cos": cosine_rows(entry.v, fresh.v)}
