@@ -32,7 +32,7 @@
 
 namespace dllm {
 
-constexpr int kMaxAttnSplits = 8;   // key shares per (sequence, head, 32 queries)
+constexpr int kMaxAttnSplits = 16;  // key shares per (sequence, head, 32 queries)
 
 struct AttnArgs {
   const void* q;      // T [rows][d]
@@ -299,15 +299,16 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   attn_finish<T, DH, NW>(a, w, mrun, lrun, o, lds);
 }
 
-// Combine the key shares of a split attention launch in share order (one
-// workgroup per (sequence, head, 32 queries)); launched after attn_kernel on
-// the same stream, so every share is complete.  256 threads: thread t handles
-// accumulator lane t%64 and the registers (i, r) with (16 i + r) % 4 == t/64.
+// Combine the key shares of a split attention launch in share order; launched
+// after attn_kernel on the same stream, so every share is complete.  Grid
+// (sequence x head x 32-query block, output d-tile of 32): wave w of the 4
+// handles accumulator registers 4w .. 4w+3 of that d-tile, so each thread
+// issues all of its loads (2 + 4 per share) before the first use.
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int nwg) {
   constexpr int ND = DH / 32;
-  constexpr int PER = ND * 16 / 4;
-  const int lane = threadIdx.x & 63, part = threadIdx.x >> 6, wg = blockIdx.x;
+  const int lane = threadIdx.x & 63, part = threadIdx.x >> 6;
+  const int wg = blockIdx.x, i = blockIdx.y;
   const int qb = wg % a.qblocks, bh = wg / a.qblocks;
   const int h = bh % a.H, b = bh / a.H;
   const int irow = qb * 32 + (lane & 31);
@@ -316,8 +317,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int nwg) {
   const size_t rec = (size_t)(ND * 16 + 2) * 64;
   const float* base = a.ws + (size_t)wg * rec;
   const size_t sstride = (size_t)nwg * rec;
-  // every load is issued before the first use (splits <= kMaxAttnSplits)
-  float mv[kMaxAttnSplits], lv[kMaxAttnSplits], ov[kMaxAttnSplits][PER];
+  float mv[kMaxAttnSplits], lv[kMaxAttnSplits], ov[kMaxAttnSplits][4];
 #pragma unroll
   for (int sp = 0; sp < kMaxAttnSplits; ++sp) {
     const bool on = sp < a.splits;
@@ -325,30 +325,25 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int nwg) {
     mv[sp] = on ? src[lane] : -INFINITY;
     lv[sp] = on ? src[64 + lane] : 0.f;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) ov[sp][q] = on ? src[128 + (4 * q + part) * 64 + lane] : 0.f;
+    for (int q = 0; q < 4; ++q) ov[sp][q] = on ? src[128 + (i * 16 + 4 * part + q) * 64 + lane] : 0.f;
   }
   float M = -INFINITY;
 #pragma unroll
   for (int sp = 0; sp < kMaxAttnSplits; ++sp) M = fmaxf(M, mv[sp]);
   const float Mz = M == -INFINITY ? 0.f : M;
-  float L = 0.f;
-  float o[PER];
-#pragma unroll
-  for (int q = 0; q < PER; ++q) o[q] = 0.f;
+  float L = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int sp = 0; sp < kMaxAttnSplits; ++sp) {
     const float f = sp < a.splits ? exp2f(mv[sp] - Mz) : 0.f;
     L += lv[sp] * f;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) o[q] += ov[sp][q] * f;
+    for (int q = 0; q < 4; ++q) o[q] += ov[sp][q] * f;
   }
   const float inv = 1.0f / L;
   T* out = static_cast<T*>(a.out);
 #pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const int ir = 4 * q + part, i = ir / 16, r = ir % 16;
-    out[packed_off<T>(m, h * DH + i * 32 + acc32_row(r, lane), a.d)] = Elem<T>::cvt(o[q] * inv);
-  }
+  for (int q = 0; q < 4; ++q)
+    out[packed_off<T>(m, h * DH + i * 32 + acc32_row(4 * part + q, lane), a.d)] = Elem<T>::cvt(o[q] * inv);
 }
 
 }  // namespace dllm

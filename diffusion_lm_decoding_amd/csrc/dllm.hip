@@ -288,6 +288,9 @@ dllm_status launch_skinny_nt(dllm_ctx* c, const Timed& tm, const GemmArgs& a, co
   }
   if (fits(2) || (a.n_tiles % 2 == 0 && a.n_tiles / 2 >= 2048))
     return launch_skinny<T, MT, 2, (MT <= 2 ? 4 : 2)>(c, tm, a, epi);
+  // one n-tile: short K (the O projection) streams best in batches of 2
+  // fragments, long K (down) in batches of 4 (measured on MI355X)
+  if (a.KT <= 128) return launch_skinny<T, MT, 1, 2>(c, tm, a, epi);
   return launch_skinny<T, MT, 1, 4>(c, tm, a, epi);
 }
 
@@ -407,7 +410,7 @@ dllm_status launch_attn(dllm_ctx* c, int layer, const Fwd& f) {
   const double M = (double)f.batch * f.nr;
   Timed tm(c, DLLM_K_ATTN, f.batch * m.n_heads * kv + 2.0 * M * m.d_model * sizeof(T), f.batch * m.n_heads * fl);
   hipLaunchKernelGGL((attn_kernel<T, DH, 4>), dim3(nwg, splits), dim3(256), 0, c->stream, a);
-  if (splits > 1) hipLaunchKernelGGL((attn_merge_kernel<T, DH>), dim3(nwg), dim3(256), 0, c->stream, a, nwg);
+  if (splits > 1) hipLaunchKernelGGL((attn_merge_kernel<T, DH>), dim3(nwg, DH / 32), dim3(256), 0, c->stream, a, nwg);
   return tm.done();
 }
 
