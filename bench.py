@@ -99,7 +99,7 @@ def main():
     if not args.no_peaks and not args.probe:
         hbm, mfma = L.dllm_probe_peaks(8 << 30)
         peaks = {"hbm_gbs": hbm, "mfma_f16_tflops": mfma,
-                 "how": "library microkernels: streaming read of 8 GiB; 16x16x32 fp16 MFMA chains from registers"}
+                 "how": "library microkernels: streaming read of 8 GiB; 32x32x16 fp16 MFMA chains from registers"}
         log(f"[bench] achievable: HBM read {hbm:.0f} GB/s, fp16 MFMA {mfma:.0f} TFLOP/s")
     b16 = None if (args.no_b16 or args.probe) else workload("llada8b_p128_g128")
     max_batch = max(w.batch, b16.batch if b16 else 0)

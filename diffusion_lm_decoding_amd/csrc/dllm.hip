@@ -824,29 +824,29 @@ dllm_status dllm_probe_peaks(uint64_t bytes, double* hbm_gbs, double* mfma_f16_t
   if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess)
     return done(fail(DLLM_ERR_DEVICE, "hipEventCreate failed"));
   if (hipMalloc(&sink, 64) != hipSuccess) return done(fail(DLLM_ERR_OOM, "hipMalloc failed"));
-  const size_t n16 = (size_t)(bytes / 16);
+  const size_t n16 = (size_t)(bytes / 16) / 2048 * 2048;   // whole 32 KiB chunks (hbm_read_kernel)
   if (hbm_gbs) {
     if (hipMalloc(&buf, n16 * 16) != hipSuccess) {
       (void)hipGetLastError();
       return done(fail(DLLM_ERR_OOM, "hipMalloc of the probe buffer failed"));
     }
     if (hipMemsetAsync(buf, 1, n16 * 16, s) != hipSuccess) return done(fail(DLLM_ERR_DEVICE, "hipMemsetAsync failed"));
-    const unsigned grid = (unsigned)prop.multiProcessorCount * 8;
     float best = 1e30f;
-    for (int rep = 0; rep < 4; ++rep) {
+    for (int rep = 0; rep < 9; ++rep) {
+      const unsigned grid = (unsigned)prop.multiProcessorCount * (2u << (rep % 3));   // 2, 4, 8 per CU
       (void)hipEventRecord(e0, s);
       hipLaunchKernelGGL(hbm_read_kernel, dim3(grid), dim3(256), 0, s, static_cast<const Frag16*>(buf), n16, sink);
       (void)hipEventRecord(e1, s);
       if (hipEventSynchronize(e1) != hipSuccess) return done(fail(DLLM_ERR_DEVICE, "probe kernel failed"));
       float ms = 0.f;
       (void)hipEventElapsedTime(&ms, e0, e1);
-      if (rep > 0 && ms < best) best = ms;
+      if (rep >= 3 && ms < best) best = ms;
     }
     *hbm_gbs = (double)n16 * 16 / (best * 1e6);
   }
   if (mfma_f16_tflops) {
-    const int iters = 20000;
-    const unsigned grid = (unsigned)prop.multiProcessorCount * 8;   // 8 waves per SIMD pair slot
+    const int iters = 10000;
+    const unsigned grid = (unsigned)prop.multiProcessorCount * 8;   // 32 waves per CU
     float best = 1e30f;
     for (int rep = 0; rep < 3; ++rep) {
       (void)hipEventRecord(e0, s);
@@ -857,7 +857,7 @@ dllm_status dllm_probe_peaks(uint64_t bytes, double* hbm_gbs, double* mfma_f16_t
       (void)hipEventElapsedTime(&ms, e0, e1);
       if (rep > 0 && ms < best) best = ms;
     }
-    const double flops = (double)grid * 4 /* waves */ * iters * 8 * (2.0 * 16 * 16 * 32);
+    const double flops = (double)grid * 4 /* waves */ * iters * 4 * (2.0 * 32 * 32 * 16);
     *mfma_f16_tflops = flops / (best * 1e9);
   }
   (void)st;

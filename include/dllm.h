@@ -300,8 +300,8 @@ dllm_status dllm_get_timing(dllm_ctx* ctx, dllm_kernel_time* out, int32_t reset)
 /* Achievable peaks on the current device, measured with the library's own
  * microkernels (no context needed): hbm_gbs = GB/s of a streaming read of
  * `bytes` bytes (a temporary device buffer; pass >= 4 GiB so the memory-side
- * cache does not hold it), mfma_f16_tflops = TFLOP/s of register-resident
- * 16x16x32 fp16 MFMA chains on every CU.  Either output may be NULL.
+ * cache does not hold it; best of three grid sizes), mfma_f16_tflops = TFLOP/s
+ * of register-resident 32x32x16 fp16 MFMA chains on every CU.  Either output may be NULL.
  * Errors: DLLM_ERR_ARG (bytes < 1 MiB), DLLM_ERR_OOM, DLLM_ERR_DEVICE. */
 dllm_status dllm_probe_peaks(uint64_t bytes, double* hbm_gbs, double* mfma_f16_tflops);
 
