@@ -299,6 +299,106 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   attn_finish<T, DH, NW>(a, w, mrun, lrun, o, lds);
 }
 
+// Many query rows (cache passes, block-diffusion steps; 16-bit caches): a
+// workgroup owns 4 consecutive 32-query blocks of one (sequence, head), one
+// per wave, and streams the key tiles its last block attends through an
+// S-stage LDS ring filled by the DMA path, so each tile is read from memory
+// once for 128 queries.  Every wave runs the online softmax of its own
+// queries over every tile (keys past a query's limit are masked), and
+// writes its normalised output; no key shares.
+template <typename T, int DH, int S>
+__global__ __launch_bounds__(256) void attn_wide_kernel(AttnArgs a) {
+  static_assert(sizeof(T) == 2, "16-bit caches");
+  constexpr int NW = 4;
+  constexpr int NQF = DH / 16, ND = DH / 32;
+  constexpr int FR = NQF + 2 * ND;   // fragments per 32-key tile: K then V^T
+  constexpr int LW = FR / NW;
+  static_assert(FR % NW == 0, "tile fragments split evenly over the waves");
+  __shared__ Frag16 ring[S][FR][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5;
+  const int qgroups = (a.qblocks + NW - 1) / NW;
+  const int qg = blockIdx.x % qgroups, bh = blockIdx.x / qgroups;
+  const int h = bh % a.H, b = bh / a.H;
+  const int qb = qg * NW + wave;                       // this wave's query block
+  const int irow = qb * 32 + (lane & 31);
+  const bool valid = irow < a.g.nr;
+  const int m = b * a.g.nr + (valid ? irow : 0);
+  const int limit = valid ? attn_limit(a, a.g.row_start + irow) : 0;
+  // the workgroup's key tiles: what its last valid query row attends
+  const int last = min(a.g.nr, qg * NW * 32 + NW * 32) - 1;
+  const int nt = (attn_limit(a, a.g.row_start + last) + 31) / 32;
+  const T* kc = static_cast<const T*>(a.kc) + ((size_t)b * a.H + h) * a.seq_pad * DH;
+  const T* vt = static_cast<const T*>(a.vt) + ((size_t)b * a.H + h) * DH * a.seq_pad;
+
+  auto issue = [&](int t) {
+    const int kb = t * 32, st = t % S;
+#pragma unroll
+    for (int q = 0; q < LW; ++q) {
+      const int f = wave + q * NW;
+      const T* src;
+      if (f < NQF) {
+        src = kc + (size_t)(kb + (lane & 31)) * DH + f * 16 + 8 * hf;
+      } else {
+        const int g = f - NQF, i = g >> 1, c = g & 1;
+        src = vt + (size_t)(i * 32 + (lane & 31)) * a.seq_pad + kb + (2 * c + hf) * 8;
+      }
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)&ring[st][f][0], 16, 0, 0);
+    }
+  };
+  auto wait_tile = [&](int ahead) {   // this wave's copies of a tile landed, `ahead` later tiles outstanding
+    switch (ahead) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<(S > 1 ? 1 : 0) * LW>(); break;
+      case 2: wait_vmcnt<(S > 2 ? 2 : 0) * LW>(); break;
+      case 3: wait_vmcnt<(S > 3 ? 3 : 0) * LW>(); break;
+      case 4: wait_vmcnt<(S > 4 ? 4 : 0) * LW>(); break;
+      case 5: wait_vmcnt<(S > 5 ? 5 : 0) * LW>(); break;
+      default: wait_vmcnt<(S > 6 ? 6 : 0) * LW>(); break;
+    }
+  };
+#pragma unroll
+  for (int t = 0; t < S; ++t)
+    if (t < nt) issue(t);
+
+  Frag16 qf[NQF];
+  const T* qrow = static_cast<const T*>(a.q) + (size_t)m * a.d + h * DH + 8 * hf;
+#pragma unroll
+  for (int c = 0; c < NQF; ++c) qf[c] = *reinterpret_cast<const Frag16*>(qrow + c * 16);
+  float mrun = -INFINITY, lrun = 0.f;
+  f32x16 o[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
+
+  for (int t = 0; t < nt; ++t) {
+    wait_tile(min(nt, t + S) - t - 1);
+    __builtin_amdgcn_s_barrier();
+    const int st = t % S;
+    Frag16 kf[NQF], vf[ND][2];
+#pragma unroll
+    for (int c = 0; c < NQF; ++c) kf[c] = ring[st][c][lane];
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) vf[i][c] = ring[st][NQF + 2 * i + c][lane];
+    attn_tile16<T, DH>(qf, kf, vf, t * 32, limit, a.scale_log2, mrun, lrun, o, lane);
+    // stage st is read by every wave before it is refilled with tile t + S
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    if (t + S < nt) issue(t + S);
+  }
+  if (!valid) return;
+  const float inv = 1.0f / lrun;
+  T* out = static_cast<T*>(a.out);
+#pragma unroll
+  for (int i = 0; i < ND; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      out[packed_off<T>(m, h * DH + i * 32 + acc32_row(r, lane), a.d)] = Elem<T>::cvt(o[i][r] * inv);
+}
+
 // Combine the key shares of a split attention launch in share order; launched
 // after attn_kernel on the same stream, so every share is complete.  Grid
 // (sequence x head x 32-query block, output d-tile of 32): wave w of the 4

@@ -311,14 +311,14 @@ dllm_status launch_big(dllm_ctx* c, const GemmArgs& a, const Epi& epi) {
     const double t = std::ceil(nwg / 256.0) * g.ntw * g.mtw / g.eff;
     if (t < best_t) { best_t = t; best = i; }
   }
-  const bool ks2 = a.KT % 2 == 0;
-  if (!ks2 && best >= 2) best = -1;  // 8x6 and 8x8 use two k-fragments per stage
+  // every configuration but the fallback takes two k-fragments per stage
+  if (a.KT % 2 != 0) best = -1;
   auto grid = [&](int ntw, int mtw) { return dim3((unsigned)(cdiv(a.n_tiles, ntw) * cdiv(a.m_tiles, mtw))); };
   switch (best) {
-    case 0: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 12, 12, 2, 4, 1, 4>), grid(12, 12), dim3(512), 0, c->stream, a, epi); break;
-    case 1: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 16, 8, 4, 2, 1, 4>), grid(16, 8), dim3(512), 0, c->stream, a, epi); break;
+    case 0: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 12, 12, 2, 4, 2, 3>), grid(12, 12), dim3(512), 0, c->stream, a, epi); break;
+    case 1: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 16, 8, 4, 2, 2, 3>), grid(16, 8), dim3(512), 0, c->stream, a, epi); break;
     case 2: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 8, 2, 2, 2, 4>), grid(8, 8), dim3(256), 0, c->stream, a, epi); break;
-    case 3: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 6, 2, 2, 2, 4>), grid(8, 6), dim3(256), 0, c->stream, a, epi); break;
+    case 3: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 6, 2, 2, 2, 5>), grid(8, 6), dim3(256), 0, c->stream, a, epi); break;
     default: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 8, 2, 2, 1, 6>), grid(8, 8), dim3(256), 0, c->stream, a, epi); break;
   }
   return DLLM_OK;
@@ -409,6 +409,15 @@ dllm_status launch_attn(dllm_ctx* c, int layer, const Fwd& f) {
   }
   const double M = (double)f.batch * f.nr;
   Timed tm(c, DLLM_K_ATTN, f.batch * m.n_heads * kv + 2.0 * M * m.d_model * sizeof(T), f.batch * m.n_heads * fl);
+  if constexpr (sizeof(T) == 2) {
+    // 128 or more query rows per sequence: 4 query blocks share each key tile
+    if (a.qblocks >= 4) {
+      a.splits = 1;
+      const int groups = f.batch * m.n_heads * cdiv(a.qblocks, 4);
+      hipLaunchKernelGGL((attn_wide_kernel<T, DH, 4>), dim3(groups), dim3(256), 0, c->stream, a);
+      return tm.done();
+    }
+  }
   hipLaunchKernelGGL((attn_kernel<T, DH, 4>), dim3(nwg, splits), dim3(256), 0, c->stream, a);
   if (splits > 1) hipLaunchKernelGGL((attn_merge_kernel<T, DH>), dim3(nwg, DH / 32), dim3(256), 0, c->stream, a, nwg);
   return tm.done();

@@ -12,6 +12,8 @@
 //    tile of up to 192x192 outputs; fragments of both operands are copied
 //    into a multi-stage LDS ring by the DMA path and shared by the waves.
 #pragma once
+#include <type_traits>
+
 #include "mfma.h"
 
 namespace dllm {
@@ -491,29 +493,73 @@ __global__ __launch_bounds__(64 * WN * WM) void gemm_big_kernel(GemmArgs a, Epi 
 #pragma unroll
     for (int i = 0; i < TM; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-  for (int st = 0; st < S - 1; ++st)
-    if (st < nst) issue(st);
-  for (int st = 0; st < nst; ++st) {
-    // stage st landed (this wave), then every wave's copies and reads of st-1
-    if (st + S - 2 < nst) wait_vmcnt<(S - 2) * LW>();
-    else wait_vmcnt<0>();
-    wait_lgkmcnt0();
-    __builtin_amdgcn_s_barrier();
-    if (st + S - 1 < nst) issue(st + S - 1);
+  // one (stage, k-fragment) step computes from one register set while the
+  // next step's fragments are read from LDS into the other
+  auto read = [&](int st, int kk, Frag16 (&wf)[TN], Frag16 (&xf)[TM]) {
     const int buf = st % S;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      Frag16 wf[TN], xf[TM];
+    for (int j = 0; j < TN; ++j) wf[j] = lds[buf][(wn * TN + j) * KS + kk][lane];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) wf[j] = lds[buf][(wn * TN + j) * KS + kk][lane];
+    for (int i = 0; i < TM; ++i) xf[i] = lds[buf][KS * NTW + (wm * TM + i) * KS + kk][lane];
+  };
+  auto mma = [&](const Frag16 (&wf)[TN], const Frag16 (&xf)[TM]) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) xf[i] = lds[buf][KS * NTW + (wm * TM + i) * KS + kk][lane];
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int i = 0; i < TM; ++i) acc[j][i] = Mfma16<T>::mma(wf[j], xf[i], acc[j][i]);
+      for (int i = 0; i < TM; ++i) acc[j][i] = Mfma16<T>::mma(wf[j], xf[i], acc[j][i]);
+  };
+  // this wave's copies of stage `st` have landed when at most `ahead` later
+  // stages are still outstanding (copies complete in issue order)
+  auto wait_stage = [&](int ahead) {
+    static_assert(S <= 8, "wait table");
+    switch (ahead) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<(S > 1 ? 1 : 0) * LW>(); break;
+      case 2: wait_vmcnt<(S > 2 ? 2 : 0) * LW>(); break;
+      case 3: wait_vmcnt<(S > 3 ? 3 : 0) * LW>(); break;
+      case 4: wait_vmcnt<(S > 4 ? 4 : 0) * LW>(); break;
+      case 5: wait_vmcnt<(S > 5 ? 5 : 0) * LW>(); break;
+      default: wait_vmcnt<(S > 6 ? 6 : 0) * LW>(); break;
     }
+  };
+  // all S buffers in flight; stage u + S is copied into buffer u % S once
+  // every wave has finished reading stage u
+#pragma unroll
+  for (int st = 0; st < S; ++st)
+    if (st < nst) issue(st);
+  wait_stage(min(nst, S) - 1);
+  __builtin_amdgcn_s_barrier();
+  // two register sets; step t = st*KS + kk computes from set t%2 (a compile-
+  // time index: stages are unrolled in pairs) while set (t+1)%2 is loaded.
+  // The loads are unconditional (the last step re-reads its own fragments)
+  // so no branch joins sit between them and the MFMAs.
+  static_assert(KS == 1 || KS == 2, "k-fragments per stage");
+  Frag16 fw[2][TN], fx[2][TM];
+  read(0, 0, fw[0], fx[0]);
+  const int nsteps = nst * KS;
+  auto do_step = [&](int st, int kk, auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value, nxt = 1 - cur;
+    const bool last = st * KS + kk + 1 == nsteps;
+    if (kk + 1 < KS) {
+      read(st, kk + 1, fw[nxt], fx[nxt]);
+    } else {
+      // next stage: its copies landed everywhere, stage st is read everywhere
+      wait_stage(last ? 0 : min(nst, st + S) - st - 2);
+      wait_lgkmcnt0();
+      __builtin_amdgcn_s_barrier();
+      if (st + S < nst) issue(st + S);
+      read(last ? st : st + 1, 0, fw[nxt], fx[nxt]);
+    }
+    mma(fw[cur], fx[cur]);
+  };
+  auto do_stage = [&](int st, auto base_c) {
+    constexpr int b0 = decltype(base_c)::value;
+    do_step(st, 0, std::integral_constant<int, b0>{});
+    if constexpr (KS == 2) do_step(st, 1, std::integral_constant<int, 1 - b0>{});
+  };
+  for (int st = 0; st < nst; st += 2) {
+    do_stage(st, std::integral_constant<int, 0>{});
+    if (st + 1 < nst) do_stage(st + 1, std::integral_constant<int, (KS & 1)>{});
   }
   if (a.ssq) {
 #pragma unroll

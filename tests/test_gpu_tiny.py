@@ -82,6 +82,20 @@ def test_bf16_lockstep(engines, cache, rule, kw):
     assert rep.max_logit_err < 5e-2 and rep.max_conf_err < 1e-2
 
 
+@pytest.mark.parametrize("cache", ["dual", "prefix", "none"])
+def test_bf16_lockstep_wide_attention(engines, cache):
+    """128-row forwards (refresh and no-cache steps) take the wide-query
+    attention kernel (4 query blocks share each key tile)."""
+    from diffusion_lm_decoding_amd.engine import Engine
+    eng, om = engines["bf16"]
+    pr, t, a = _inputs(2, 64, 64, seed=33, alpha_max=16.0)
+    cfg = Engine.decode_cfg(2, 64, 64, 16, cache=cache)
+    cv = eng.canvas(pr, t, a, 64)
+    rep = replay(eng, cv, cfg, om, pr, t, a, cache, "threshold", tol=Tol(fp32=False), seq=1, max_steps=12)
+    assert not rep.bad, rep.bad[:5]
+    assert rep.max_logit_err < 5e-2 and rep.max_conf_err < 1e-2
+
+
 def test_batch_equals_single_runs(engines):
     from diffusion_lm_decoding_amd.engine import Engine
     eng, om = engines["f32"]
