@@ -300,16 +300,15 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
 }
 
 // Many query rows (cache passes, block-diffusion steps; 16-bit caches): a
-// workgroup owns 4 consecutive 32-query blocks of one (sequence, head), one
+// workgroup owns NW consecutive 32-query blocks of one (sequence, head), one
 // per wave, and streams the key tiles its last block attends through an
 // S-stage LDS ring filled by the DMA path, so each tile is read from memory
-// once for 128 queries.  Every wave runs the online softmax of its own
+// once for 32 NW queries.  Every wave runs the online softmax of its own
 // queries over every tile (keys past a query's limit are masked), and
 // writes its normalised output; no key shares.
-template <typename T, int DH, int S>
-__global__ __launch_bounds__(256) void attn_wide_kernel(AttnArgs a) {
+template <typename T, int DH, int NW, int S>
+__global__ __launch_bounds__(64 * NW) void attn_wide_kernel(AttnArgs a) {
   static_assert(sizeof(T) == 2, "16-bit caches");
-  constexpr int NW = 4;
   constexpr int NQF = DH / 16, ND = DH / 32;
   constexpr int FR = NQF + 2 * ND;   // fragments per 32-key tile: K then V^T
   constexpr int LW = FR / NW;

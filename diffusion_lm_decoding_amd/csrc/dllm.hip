@@ -410,11 +410,17 @@ dllm_status launch_attn(dllm_ctx* c, int layer, const Fwd& f) {
   const double M = (double)f.batch * f.nr;
   Timed tm(c, DLLM_K_ATTN, f.batch * m.n_heads * kv + 2.0 * M * m.d_model * sizeof(T), f.batch * m.n_heads * fl);
   if constexpr (sizeof(T) == 2) {
-    // 128 or more query rows per sequence: 4 query blocks share each key tile
+    // 128 or more query rows per sequence: 4 query blocks share each key
+    // tile, 2 when 4 would leave most CUs idle
     if (a.qblocks >= 4) {
       a.splits = 1;
-      const int groups = f.batch * m.n_heads * cdiv(a.qblocks, 4);
-      hipLaunchKernelGGL((attn_wide_kernel<T, DH, 4>), dim3(groups), dim3(256), 0, c->stream, a);
+      const int g4 = f.batch * m.n_heads * cdiv(a.qblocks, 4);
+      if (g4 >= 256) {
+        hipLaunchKernelGGL((attn_wide_kernel<T, DH, 4, 4>), dim3(g4), dim3(256), 0, c->stream, a);
+      } else {
+        const int g2 = f.batch * m.n_heads * cdiv(a.qblocks, 2);
+        hipLaunchKernelGGL((attn_wide_kernel<T, DH, 2, 4>), dim3(g2), dim3(128), 0, c->stream, a);
+      }
       return tm.done();
     }
   }

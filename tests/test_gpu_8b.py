@@ -21,7 +21,7 @@ from .parity import Report, Tol, compare_step, replay
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
-MAX_BATCH, MAX_SEQ = 16, 2048
+MAX_BATCH, MAX_SEQ = 16, 3072
 
 
 @pytest.fixture(scope="module")
@@ -159,6 +159,23 @@ def test_block_causal_lockstep(big):
     cv = eng.canvas(pr, t, a, 512)
     _check(replay(eng, cv, cfg, om, pr, t, a, "block_causal", "threshold", tol=Tol(fp32=False), seq=1,
                   max_steps=2), "block_causal")
+
+
+def test_block_diffusion_full_size_first_step(big):
+    """The block-diffusion workload at full size (batch 8, P 2048, L 1024,
+    blocks of 256): the GPU's prompt pass over 8 x 2048 rows and first
+    block-causal step over 8 x 256 rows; sequence 0 checked against the
+    oracle's own prompt pass and step."""
+    from diffusion_lm_decoding_amd.engine import Engine
+    eng, om = big
+    w = workload("llada8b_blockdiff")
+    pr = gen_prompt(LLADA_8B, w.batch, w.prompt_len, w.prompt_seed)
+    t, a = gen_bias(LLADA_8B, w.batch, w.gen_len, w.bias_seed, w.alpha_max)
+    cfg = Engine.cfg_from_workload(w)
+    assert (cfg.batch, cfg.prompt_len, cfg.gen_len, cfg.block_len) == (8, 2048, 1024, 256)
+    cv = eng.canvas(pr, t, a, w.gen_len)
+    _check(replay(eng, cv, cfg, om, pr, t, a, "block_causal", w.rule, tau=w.tau, tol=Tol(fp32=False), seq=0,
+                  max_steps=1), "block diffusion, full size")
 
 
 def test_long_canvas_decode_properties(big):
