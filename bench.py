@@ -9,7 +9,9 @@ bias) are synthetic and already resident in HBM when timing starts.
 Prints one JSON line.  `roofline` is computed for the kernel class with the
 largest device time in the denoising steps, from the library's algorithmic
 byte/flop counts and the HIP-event durations of that class's launches inside
-the timed region (events on the library's stream).  `cpu_baseline` times the
+the timed region (events on the library's stream, on every 31st launch of the
+class: 31 is coprime to the 32 layers, so the sample rotates over them, and
+the events' own few-microsecond cost stays out of the throughput).  `cpu_baseline` times the
 float64 oracle on a bounded sample of the same workload on the host cores.
 """
 from __future__ import annotations
@@ -24,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+TIMED_SAMPLE_EVERY = 31
 # HBM bytes per launch of the dominant kernel from two rocprofv3 --pmc runs
 # (FETCH_SIZE, WRITE_SIZE, calibrated on a copy of known size), valid only
 # while the kernel sources hash to the value recorded with them
@@ -125,8 +128,9 @@ def main():
     kernel_table("cache-pass kernels (warmup)", prof["cache"])
     dom = max(prof["step"], key=lambda k: prof["step"][k]["ms"])
 
-    # timed region: only the dominant class is bracketed by events
-    L.dllm_set_timing(eng.ctx, [dom])
+    # timed region: a rotating sample of the dominant class's launches is
+    # bracketed by events
+    L.dllm_set_timing(eng.ctx, [dom], TIMED_SAMPLE_EVERY)
     torch.cuda.synchronize(dev)
     t_start = time.perf_counter()
     stats = [eng.decode(canvases[args.warmup + i], cfg) for i in range(args.steps)]
@@ -153,7 +157,7 @@ def main():
     roof.update(frac=roof["achieved"] / roof["peak"], traffic=stored_traffic(w.name, dom),
                 traffic_unit="HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 kernel=f"{dom} projection (denoising step)",
-                launches=kt["launches"], us_per_launch=1e3 * kt["ms"] / n,
+                launches=kt["launches"], sampled_every=TIMED_SAMPLE_EVERY, us_per_launch=1e3 * kt["ms"] / n,
                 bytes_per_launch=kt["bytes"] / n, flops_per_launch=kt["flops"] / n)
 
     out = {

@@ -87,7 +87,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.dllm_probe_peaks.restype = C.c_int
     lib.dllm_decode.argtypes = [P, C.POINTER(Canvas), C.POINTER(DecodeCfg), C.POINTER(Stats)]
     lib.dllm_decode.restype = C.c_int
-    lib.dllm_set_timing.argtypes = [P, C.c_uint32]
+    lib.dllm_set_timing.argtypes = [P, C.c_uint32, C.c_uint32]
     lib.dllm_set_timing.restype = C.c_int
     lib.dllm_get_timing.argtypes = [P, C.POINTER(KernelTime), C.c_int32]
     lib.dllm_get_timing.restype = C.c_int
@@ -147,11 +147,11 @@ def dllm_probe_peaks(nbytes: int = 8 << 30):
     return hbm.value, mfma.value
 
 
-def dllm_set_timing(ctx: int, classes) -> None:
+def dllm_set_timing(ctx: int, classes, sample_every: int = 1) -> None:
     mask = 0
     for c in classes:
         mask |= 1 << KERNEL_CLASSES.index(c)
-    check(load().dllm_set_timing(C.c_void_p(ctx), mask))
+    check(load().dllm_set_timing(C.c_void_p(ctx), mask, sample_every))
 
 
 def dllm_get_timing(ctx: int, reset: bool = True) -> dict:

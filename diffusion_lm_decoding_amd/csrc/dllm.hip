@@ -110,6 +110,8 @@ struct dllm_ctx {
   // kernel timing (dllm_set_timing): event pairs pending until the next read
   struct Pending { int cls; hipEvent_t a, b; double bytes, flops; };
   uint32_t timing_mask = 0;
+  uint32_t timing_every = 1;  // time one launch in this many of each class
+  uint64_t timing_count[2 * DLLM_K_COUNT] = {};
   int timing_slot = 0;        // 0 during denoising steps, DLLM_K_COUNT during cache passes
   std::vector<Pending> pending;
   std::vector<hipEvent_t> event_pool;
@@ -182,10 +184,13 @@ struct Timed {
   int cls;
   double bytes, flops;
   bool ext;
+  bool on = false;
   hipEvent_t a = nullptr, b = nullptr;
   Timed(dllm_ctx* c_, int cls_, double by, double fl, bool ext_ = false)
       : c(c_), cls(cls_), bytes(by), flops(fl), ext(ext_) {
-    if ((c->timing_mask >> cls) & 1u) {
+    if ((c->timing_mask >> cls) & 1u)
+      on = c->timing_count[cls + c->timing_slot]++ % c->timing_every == 0;
+    if (on) {
       a = c->get_event();
       b = c->get_event();
       if (!a || !b) a = b = nullptr;  // reported by done()
@@ -194,11 +199,8 @@ struct Timed {
   }
   dllm_status done() {
     TRY(check_launch());
-    if ((c->timing_mask >> cls) & 1u) {
-      if (!a) return fail(DLLM_ERR_DEVICE, "hipEventCreate failed");
-    } else {
-      return DLLM_OK;
-    }
+    if (!on) return DLLM_OK;
+    if (!a) return fail(DLLM_ERR_DEVICE, "hipEventCreate failed");
     if (!ext) HIPCHK(hipEventRecord(b, c->stream));
     c->pending.push_back({cls + c->timing_slot, a, b, bytes, flops});
     if (c->pending.size() >= 4096) {
@@ -799,10 +801,13 @@ dllm_status dllm_init_weights(dllm_ctx** out, const dllm_model_cfg* cfg, const v
   return DLLM_OK;
 }
 
-dllm_status dllm_set_timing(dllm_ctx* ctx, uint32_t class_mask) {
+dllm_status dllm_set_timing(dllm_ctx* ctx, uint32_t class_mask, uint32_t sample_every) {
   g_err.clear();
   if (!ctx) return fail(DLLM_ERR_ARG, "ctx is NULL");
+  if (sample_every < 1) return fail(DLLM_ERR_ARG, "sample_every must be >= 1");
   ctx->timing_mask = class_mask & ((1u << DLLM_K_COUNT) - 1u);
+  ctx->timing_every = sample_every;
+  for (auto& n : ctx->timing_count) n = 0;
   return DLLM_OK;
 }
 

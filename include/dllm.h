@@ -284,11 +284,16 @@ typedef struct {
   double flops;       /* summed algorithmic floating-point operations              */
 } dllm_kernel_time;
 
-/* Bracket every later launch of the kernel classes in class_mask (bit i =
+/* Bracket later launches of the kernel classes in class_mask (bit i =
  * class i) with HIP events on the context's stream; 0 turns timing off.
- * Counters accumulate until read with reset = 1.
- * Errors: DLLM_ERR_ARG (ctx NULL). */
-dllm_status dllm_set_timing(dllm_ctx* ctx, uint32_t class_mask);
+ * Of each class's launches (counted separately for denoising steps and cache
+ * passes, from this call on) the 1st, (1+sample_every)th, ... are timed:
+ * sample_every = 1 times them all.  The events themselves lengthen the gaps
+ * around a timed launch by a few microseconds, so a throughput measurement
+ * samples (e.g. 31, coprime to the layer count, so the sample rotates over
+ * the layers).  Counters accumulate until read with reset = 1.
+ * Errors: DLLM_ERR_ARG (ctx NULL, sample_every 0). */
+dllm_status dllm_set_timing(dllm_ctx* ctx, uint32_t class_mask, uint32_t sample_every);
 
 /* Wait for the stream, then copy the counters to out, a host array of
  * 2 * DLLM_K_COUNT entries: [0, DLLM_K_COUNT) for launches made by
