@@ -200,3 +200,93 @@ def test_long_canvas_decode_properties(big):
         blk = cs[0, j * 32:(j + 1) * 32]
         assert blk.max() - blk.min() < 32
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("k", [1, 4])
+def test_fixed_count_rules_lockstep(big, k):
+    """Benchmark shape (P 512, L 256, B 32), DualCache, a fixed k tokens per
+    step (top-k by confidence)."""
+    from diffusion_lm_decoding_amd.engine import Engine
+    eng, om = big
+    pr, t, a = _inputs(1, 512, 256, seed=2401 + k, alpha_max=12.0)
+    cfg = Engine.decode_cfg(1, 512, 256, 32, cache="dual", rule="topk", k=k)
+    cv = eng.canvas(pr, t, a, 256)
+    _check(replay(eng, cv, cfg, om, pr, t, a, "dual", "topk", k=k, tol=Tol(fp32=False), max_steps=2),
+           f"top-{k}")
+
+
+@pytest.mark.parametrize("batch", [4, 8])
+def test_batch_4_and_8_first_step(big, batch):
+    """Batch shapes between 1 and 16 (P 128, L 128, B 32): the step has
+    batch x 32 rows; the first and last sequences are checked."""
+    from diffusion_lm_decoding_amd.engine import Engine
+    eng, om = big
+    w = workload("llada8b_p128_g128", alpha_max=24.0)
+    pr = gen_prompt(LLADA_8B, batch, 128, w.prompt_seed + batch)
+    t, a = gen_bias(LLADA_8B, batch, 128, w.bias_seed + batch, w.alpha_max)
+    cfg = Engine.decode_cfg(batch, 128, 128, 32, cache="dual")
+    cv = eng.canvas(pr, t, a, 128)
+    eng.refresh(cv, cfg)
+    before = cv.tokens.cpu().numpy()
+    _, _, gconf, gtok, glog = eng.step(cv, cfg, 0, debug=True, debug_logits=True)
+    after = cv.tokens.cpu().numpy()
+    rep = Report()
+    dec = OracleDecoder(om, 128, 128, 32, cache="dual")
+    for b in (0, batch - 1):
+        st = dec.new_state(pr[b], t[b], a[b])
+        st.canvas[:] = before[b]
+        dec.refresh(st)
+        cand, y, c, l = dec.evaluate(st, 0)
+        rows = b * 32 + (cand - 128)
+        compare_step(rep, Tol(fp32=False), dec, cand, y, c, l, gconf.cpu().numpy()[rows].astype(np.float64),
+                     gtok.cpu().numpy()[rows], glog.cpu().numpy()[rows].astype(np.float64), before[b], after[b],
+                     tag=f"batch {batch} sequence {b}")
+    _check(rep, f"batch {batch}")
+
+
+def test_long_canvas_block0_exact_point(big):
+    """Long canvas (P 1024, L 1024, B 32), right after the first refresh:
+    the DualCache step under threshold 0.9 and the factor rule with f = 1 and
+    2, and the PrefixCache step (1024 recomputed rows), each from the same
+    refreshed canvas, against one oracle refresh."""
+    from diffusion_lm_decoding_amd.engine import Engine
+    eng, om = big
+    w = workload("llada8b_p1024_g1024", alpha_max=24.0)
+    pr = gen_prompt(LLADA_8B, 1, w.prompt_len, w.prompt_seed)
+    t, a = gen_bias(LLADA_8B, 1, w.gen_len, w.bias_seed, w.alpha_max)
+    P, Lg = w.prompt_len, w.gen_len
+    cv = eng.canvas(pr, t, a, Lg)
+    start = cv.tokens.clone()
+    dual = OracleDecoder(om, P, Lg, 32, cache="dual")
+    st = dual.new_state(pr[0], t[0], a[0])
+    dual.refresh(st)
+    cand, y, c, l = dual.evaluate(st, 0)
+    rep = Report()
+    for rule, kw in (("threshold", dict(tau=0.9)), ("factor", dict(factor=1.0)), ("factor", dict(factor=2.0))):
+        cv.tokens.copy_(start)
+        cfg = Engine.decode_cfg(1, P, Lg, 32, cache="dual", rule=rule, **kw)
+        eng.begin(cv, cfg)
+        eng.refresh(cv, cfg)
+        before = cv.tokens.cpu().numpy()[0]
+        _, _, gconf, gtok, glog = eng.step(cv, cfg, 0, debug=True, debug_logits=True)
+        after = cv.tokens.cpu().numpy()[0]
+        rows = cand - P
+        dec = OracleDecoder(om, P, Lg, 32, cache="dual", rule=rule, **kw)
+        compare_step(rep, Tol(fp32=False), dec, cand, y, c, l, gconf.cpu().numpy()[rows].astype(np.float64),
+                     gtok.cpu().numpy()[rows], glog.cpu().numpy()[rows].astype(np.float64), before, after,
+                     tag=f"dual {rule} {kw}")
+    prefix = OracleDecoder(om, P, Lg, 32, cache="prefix")
+    cand, y, c, l = prefix.evaluate(st, 0)
+    cv.tokens.copy_(start)
+    cfg = Engine.decode_cfg(1, P, Lg, 32, cache="prefix")
+    eng.begin(cv, cfg)
+    eng.refresh(cv, cfg)
+    before = cv.tokens.cpu().numpy()[0]
+    _, _, gconf, gtok, glog = eng.step(cv, cfg, 0, debug=True, debug_logits=True)
+    after = cv.tokens.cpu().numpy()[0]
+    rows = cand - P
+    compare_step(rep, Tol(fp32=False), prefix, cand, y, c, l, gconf.cpu().numpy()[rows].astype(np.float64),
+                 gtok.cpu().numpy()[rows], glog.cpu().numpy()[rows].astype(np.float64), before, after,
+                 tag="prefix threshold")
+    _check(rep, "long canvas, block 0")
+    assert rep.steps == 4
