@@ -297,17 +297,20 @@ dllm_status launch_skinny_nt(dllm_ctx* c, const Timed& tm, const GemmArgs& a, co
 }
 
 // Large-M tile shapes (NTW x MTW 16x16 tiles per workgroup), measured on
-// MI355X for the LLaDA-8B cache-pass and batch-16 shapes; eff is the relative
-// throughput of one busy CU.
+// MI355X for the LLaDA-8B cache-pass, batch-16 and block-diffusion shapes;
+// eff is the relative throughput of one busy CU.  192 columns x 256 rows
+// fills one round exactly at 512 rows (gate/up: 147 -> 96 us) and four
+// rounds at 2048.
 struct BigCfg { int ntw, mtw; double eff; };
-constexpr BigCfg kBigCfgs[] = {{12, 12, 1.0}, {16, 8, 0.85}, {8, 8, 0.75}, {8, 6, 0.72}};
+constexpr BigCfg kBigCfgs[] = {{12, 12, 1.0}, {16, 8, 0.85}, {8, 8, 0.75}, {8, 6, 0.72}, {12, 16, 1.05}};
+constexpr int kNumBigCfgs = sizeof(kBigCfgs) / sizeof(kBigCfgs[0]);
 
 template <typename T, class Epi>
 dllm_status launch_big(dllm_ctx* c, const GemmArgs& a, const Epi& epi) {
   // estimated time ~ rounds of 256 workgroups x tile area / eff
   int best = 0;
   double best_t = 1e300;
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kNumBigCfgs; ++i) {
     const BigCfg& g = kBigCfgs[i];
     const double nwg = (double)cdiv(a.n_tiles, g.ntw) * cdiv(a.m_tiles, g.mtw);
     const double t = std::ceil(nwg / 256.0) * g.ntw * g.mtw / g.eff;
@@ -321,6 +324,7 @@ dllm_status launch_big(dllm_ctx* c, const GemmArgs& a, const Epi& epi) {
     case 1: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 16, 8, 4, 2, 2, 3>), grid(16, 8), dim3(512), 0, c->stream, a, epi); break;
     case 2: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 8, 2, 2, 2, 4>), grid(8, 8), dim3(256), 0, c->stream, a, epi); break;
     case 3: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 6, 2, 2, 2, 5>), grid(8, 6), dim3(256), 0, c->stream, a, epi); break;
+    case 4: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 12, 16, 2, 4, 2, 2>), grid(12, 16), dim3(512), 0, c->stream, a, epi); break;
     default: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 8, 2, 2, 1, 6>), grid(8, 8), dim3(256), 0, c->stream, a, epi); break;
   }
   return DLLM_OK;
