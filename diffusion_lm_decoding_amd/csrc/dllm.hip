@@ -93,6 +93,8 @@ struct dllm_ctx {
   float* ssq_head = nullptr;  // [d/16][max_head] same for the LM-head rows
   float* rstd = nullptr;      // [rstd_rows] per-row 1/rms for the large-M projections
   int rstd_rows = 0;
+  float* gemm_part = nullptr; // K-split partial tiles of the large-M projections
+  size_t gemm_part_floats = 0;
   float* attn_ws = nullptr;
   size_t attn_ws_floats = 0;
 
@@ -305,20 +307,41 @@ struct BigCfg { int ntw, mtw; double eff; };
 constexpr BigCfg kBigCfgs[] = {{12, 12, 1.0}, {16, 8, 0.85}, {8, 8, 0.75}, {8, 6, 0.72}, {12, 16, 1.05}};
 constexpr int kNumBigCfgs = sizeof(kBigCfgs) / sizeof(kBigCfgs[0]);
 
+// K splits of a large-M projection: when the best tile leaves most CUs
+// idle (few output tiles, long K: the down and O projections at 128-512
+// rows), the K range is split over 2-4 workgroups per tile whose fp32 partial
+// tiles are added, in split order, by gemm_split_reduce_kernel, which also
+// runs the epilogue.  Estimated time (us, fitted to MI355X sweeps of the
+// LLaDA-8B shapes): rounds of 256 workgroups x tile area x k-fragments per
+// split x 4.3 ns / eff, plus for splits the partial tiles written and read
+// back at ~6 TB/s (they largely stay in the memory-side cache) and one more
+// launch.
+constexpr int kMaxKSplits = 4;
+constexpr int kMinStagesPerSplit = 16;
+
 template <typename T, class Epi>
-dllm_status launch_big(dllm_ctx* c, const GemmArgs& a, const Epi& epi) {
-  // estimated time ~ rounds of 256 workgroups x tile area / eff
-  int best = 0;
+dllm_status launch_big(dllm_ctx* c, GemmArgs a, const Epi& epi) {
+  int best = 0, best_s = 1;
   double best_t = 1e300;
   for (int i = 0; i < kNumBigCfgs; ++i) {
     const BigCfg& g = kBigCfgs[i];
     const double nwg = (double)cdiv(a.n_tiles, g.ntw) * cdiv(a.m_tiles, g.mtw);
-    const double t = std::ceil(nwg / 256.0) * g.ntw * g.mtw / g.eff;
-    if (t < best_t) { best_t = t; best = i; }
+    for (int sp = 1; sp <= kMaxKSplits; ++sp) {
+      if (sp > 1 && (a.KT / 2 < sp * kMinStagesPerSplit ||
+                     (size_t)sp * a.m_tiles * a.n_tiles * 256 > c->gemm_part_floats))
+        break;
+      const double part_bytes = sp > 1 ? 8.0 * sp * a.m_tiles * 16.0 * a.n_tiles * 16.0 : 0.0;
+      const double t = std::ceil(nwg * sp / 256.0) * g.ntw * g.mtw * ((double)a.KT / sp) * 4.3e-3 / g.eff +
+                       (sp > 1 ? part_bytes / 6.0e6 + 3.0 : 0.0);
+      if (t < best_t) { best_t = t; best = i; best_s = sp; }
+    }
   }
   // every configuration but the fallback takes two k-fragments per stage
-  if (a.KT % 2 != 0) best = -1;
-  auto grid = [&](int ntw, int mtw) { return dim3((unsigned)(cdiv(a.n_tiles, ntw) * cdiv(a.m_tiles, mtw))); };
+  if (a.KT % 2 != 0) { best = -1; best_s = 1; }
+  a.k_splits = best_s;
+  a.part = c->gemm_part;
+  const unsigned sp = (unsigned)best_s;
+  auto grid = [&](int ntw, int mtw) { return dim3((unsigned)(cdiv(a.n_tiles, ntw) * cdiv(a.m_tiles, mtw)) * sp); };
   switch (best) {
     case 0: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 12, 12, 2, 4, 2, 3>), grid(12, 12), dim3(512), 0, c->stream, a, epi); break;
     case 1: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 16, 8, 4, 2, 2, 3>), grid(16, 8), dim3(512), 0, c->stream, a, epi); break;
@@ -327,6 +350,9 @@ dllm_status launch_big(dllm_ctx* c, const GemmArgs& a, const Epi& epi) {
     case 4: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 12, 16, 2, 4, 2, 2>), grid(12, 16), dim3(512), 0, c->stream, a, epi); break;
     default: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 8, 2, 2, 1, 6>), grid(8, 8), dim3(256), 0, c->stream, a, epi); break;
   }
+  if (best_s > 1)
+    hipLaunchKernelGGL(gemm_split_reduce_kernel<Epi>, dim3((unsigned)cdiv(a.m_tiles * a.n_tiles, 4)), dim3(256), 0,
+                       c->stream, a, epi);
   return DLLM_OK;
 }
 
@@ -754,6 +780,8 @@ dllm_status init_impl(dllm_ctx* c, const void* const* t) {
   TRY(c->alloc(&c->tok, (size_t)c->max_head * sizeof(int)));
   c->attn_ws_floats = (size_t)16 << 20;
   TRY(c->alloc(&c->attn_ws, c->attn_ws_floats * sizeof(float)));
+  c->gemm_part_floats = (size_t)16 << 20;
+  TRY(c->alloc(&c->gemm_part, c->gemm_part_floats * sizeof(float)));
   TRY(c->alloc(&c->d_stat, (2 * (size_t)m.max_batch + 4) * sizeof(int)));
   c->d_ncommit = c->d_stat;
   c->d_done = c->d_stat + m.max_batch;

@@ -242,6 +242,13 @@ struct GemmArgs {
   // gemm_big_kernel: per-row 1/rms computed beforehand by rstd_kernel
   // (required there when ssq is set)
   const float* rstd;
+  // gemm_big_kernel split over K: with k_splits > 1, workgroup group s of
+  // the grid (s slowest) sums k-stages [nst*s/k_splits, nst*(s+1)/k_splits)
+  // and stores its raw 16x16 tiles to part[s][m_tile][n_tile][lane][4]
+  // (fp32); gemm_split_reduce_kernel adds them in split order and runs the
+  // epilogue.
+  int k_splits;
+  float* part;
 };
 
 // Workgroup i runs on XCD i % 8; map consecutive logical ids to one XCD so the
@@ -460,11 +467,16 @@ __global__ __launch_bounds__(64 * WN * WM) void gemm_big_kernel(GemmArgs a, Epi 
   __shared__ Frag16 lds[S][F][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m_wg = (a.m_tiles + MTW - 1) / MTW;
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int lin_all = xcd_remap(blockIdx.x, gridDim.x);
+  const int k_splits = a.k_splits > 1 ? a.k_splits : 1;
+  const int per_split = gridDim.x / k_splits;
+  const int split = lin_all / per_split, lin = lin_all % per_split;
   const int wg_m = lin % m_wg, wg_n = lin / m_wg;   // m fastest: neighbours share the weight tile
   const int nt0 = wg_n * NTW, mt0 = wg_m * MTW;
   const int wn = wave % WN, wm = wave / WN;
-  const int nst = a.KT / KS;
+  const int nst_all = a.KT / KS;
+  const int st_first = (int)((long)nst_all * split / k_splits);
+  const int nst = (int)((long)nst_all * (split + 1) / k_splits) - st_first;
 
   // this wave's copies: fragment f = wave + q * NWAVE of each stage
   const Frag16* src[LW];
@@ -476,7 +488,7 @@ __global__ __launch_bounds__(64 * WN * WM) void gemm_big_kernel(GemmArgs a, Epi 
     const int ff = isw ? f : f - KS * NTW;
     const int tile = ff / KS, kk = ff % KS;
     const int t = isw ? min(nt0 + tile, a.n_tiles - 1) : min(mt0 + tile, a.m_tiles - 1);
-    src[q] = (isw ? a.W : a.X) + ((size_t)t * a.KT + kk) * 64 + lane;
+    src[q] = (isw ? a.W : a.X) + ((size_t)t * a.KT + (size_t)st_first * KS + kk) * 64 + lane;
     soff[q] = f;
   }
   auto issue = [&](int st) {
@@ -561,6 +573,22 @@ __global__ __launch_bounds__(64 * WN * WM) void gemm_big_kernel(GemmArgs a, Epi 
     do_stage(st, std::integral_constant<int, 0>{});
     if (st + 1 < nst) do_stage(st + 1, std::integral_constant<int, (KS & 1)>{});
   }
+  if (k_splits > 1) {
+    // raw partial tiles; the reduce kernel scales by 1/rms and runs the epilogue
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int nt = nt0 + wn * TN + j;
+      if (nt >= a.n_tiles) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int mt = mt0 + wm * TM + i;
+        if (mt < a.m_tiles)
+          *reinterpret_cast<f32x4*>(a.part + ((((size_t)split * a.m_tiles + mt) * a.n_tiles + nt) * 64 + lane) * 4) =
+              acc[j][i];
+      }
+    }
+    return;
+  }
   if (a.ssq) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -579,6 +607,30 @@ __global__ __launch_bounds__(64 * WN * WM) void gemm_big_kernel(GemmArgs a, Epi 
       if (mt < a.m_tiles) epi(nt, mt, acc[j][i], lane);
     }
   }
+}
+
+// Second half of a K-split gemm_big_kernel launch: one wave per 16x16 output
+// tile adds the k_splits partial tiles in split order (so results are
+// run-to-run identical), applies the row's 1/rms and runs the epilogue
+// exactly once.  Grid: ceil(m_tiles * n_tiles / 4) workgroups of 4 waves.
+template <class Epi>
+__global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs a, Epi epi) {
+  const int lane = threadIdx.x & 63;
+  const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tile >= a.m_tiles * a.n_tiles) return;
+  const int mt = tile / a.n_tiles, nt = tile % a.n_tiles;
+  const size_t stride = (size_t)a.m_tiles * a.n_tiles * 256;
+  const float* p = a.part + ((size_t)tile * 64 + lane) * 4;
+  f32x4 parts[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    if (s < a.k_splits) parts[s] = *reinterpret_cast<const f32x4*>(p + s * stride);
+  f32x4 v = parts[0];
+#pragma unroll
+  for (int s = 1; s < 8; ++s)
+    if (s < a.k_splits) v += parts[s];
+  if (a.ssq) v *= a.rstd[min(mt * 16 + (lane & 15), a.ssq_ld - 1)];
+  epi(nt, mt, v, lane);
 }
 
 }  // namespace dllm
