@@ -442,12 +442,17 @@ dllm_status launch_attn(dllm_ctx* c, int layer, const Fwd& f) {
   const double M = (double)f.batch * f.nr;
   Timed tm(c, DLLM_K_ATTN, f.batch * m.n_heads * kv + 2.0 * M * m.d_model * sizeof(T), f.batch * m.n_heads * fl);
   if constexpr (sizeof(T) == 2) {
-    // 128 or more query rows per sequence: 4 query blocks share each key
-    // tile, 2 when 4 would leave most CUs idle
+    // 128 or more query rows per sequence: 8 query blocks share each key
+    // tile (block-diffusion steps 190 -> 156 us per layer at batch 8), 4 or 2
+    // when more would leave most CUs idle
     if (a.qblocks >= 4) {
       a.splits = 1;
+      const int g8 = f.batch * m.n_heads * cdiv(a.qblocks, 8);
       const int g4 = f.batch * m.n_heads * cdiv(a.qblocks, 4);
-      if (g4 >= 256) {
+      constexpr bool fr8 = (DH / 16 + 2 * (DH / 32)) % 8 == 0;  // tile fragments split over 8 waves
+      if (fr8 && g8 >= 256) {
+        if constexpr (fr8) hipLaunchKernelGGL((attn_wide_kernel<T, DH, 8, 4>), dim3(g8), dim3(512), 0, c->stream, a);
+      } else if (g4 >= 256) {
         hipLaunchKernelGGL((attn_wide_kernel<T, DH, 4, 4>), dim3(g4), dim3(256), 0, c->stream, a);
       } else {
         const int g2 = f.batch * m.n_heads * cdiv(a.qblocks, 2);
