@@ -76,8 +76,9 @@ def kernel_table(title, prof):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              f"(the multi-GPU sharding plan is described in DESIGN.md).", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the library runs the "
+              f"decoding path on a single GPU (batch rows or heads would be split across GPUs, one "
+              f"process each, but no multi-GPU path is implemented).", file=sys.stderr)
         sys.exit(2)
     import torch
 
