@@ -91,6 +91,12 @@ struct dllm_ctx {
   int* tok = nullptr;
   float* ssq = nullptr;       // [d/16][max_rows] partial sums of x^2 of the residual rows
   float* ssq_head = nullptr;  // [d/16][max_head] same for the LM-head rows
+  // LM head over the still-masked rows only (more than 64 block rows): their
+  // block-row indices, their count, and the gathered packed rows / partials
+  int* head_rowmap = nullptr; // [max_head]
+  int* head_count = nullptr;  // [1]
+  void* xc = nullptr;         // like xh
+  float* ssq_c = nullptr;     // like ssq_head
   float* rstd = nullptr;      // [rstd_rows] per-row 1/rms for the large-M projections
   int rstd_rows = 0;
   float* gemm_part = nullptr; // K-split partial tiles of the large-M projections
@@ -318,6 +324,11 @@ constexpr int kNumBigCfgs = sizeof(kBigCfgs) / sizeof(kBigCfgs[0]);
 // launch.
 constexpr int kMaxKSplits = 4;
 constexpr int kMinStagesPerSplit = 16;
+// The Q/K/V epilogue (rotary, scattered cache writes) costs the reduce kernel
+// more than the estimate allows (measured at 512 rows: 63 + 30 us split
+// against 77 us unsplit), so that projection is never split.
+template <class Epi> constexpr bool kSplitOk = true;
+template <typename T> constexpr bool kSplitOk<EpiQKV<T>> = false;
 
 template <typename T, class Epi>
 dllm_status launch_big(dllm_ctx* c, GemmArgs a, const Epi& epi) {
@@ -327,7 +338,7 @@ dllm_status launch_big(dllm_ctx* c, GemmArgs a, const Epi& epi) {
     const BigCfg& g = kBigCfgs[i];
     const double nwg = (double)cdiv(a.n_tiles, g.ntw) * cdiv(a.m_tiles, g.mtw);
     for (int sp = 1; sp <= kMaxKSplits; ++sp) {
-      if (sp > 1 && (a.KT / 2 < sp * kMinStagesPerSplit ||
+      if (sp > 1 && (!kSplitOk<Epi> || a.KT / 2 < sp * kMinStagesPerSplit ||
                      (size_t)sp * a.m_tiles * a.n_tiles * 256 > c->gemm_part_floats))
         break;
       const double part_bytes = sp > 1 ? 8.0 * sp * a.m_tiles * 16.0 * a.n_tiles * 16.0 : 0.0;
@@ -360,9 +371,10 @@ dllm_status launch_big(dllm_ctx* c, GemmArgs a, const Epi& epi) {
 // X then holds x * gain and the kernel applies the per-row 1/rms.
 template <typename T, class Epi>
 dllm_status launch_gemm(dllm_ctx* c, int cls, const void* X, const void* W, int M, int N, int K, const Epi& epi,
-                        const float* ssq = nullptr, int ssq_ld = 0) {
+                        const float* ssq = nullptr, int ssq_ld = 0, const int* m_count = nullptr) {
   GemmArgs a{};
   a.X = static_cast<const Frag16*>(X);
+  a.m_count = m_count;
   a.W = static_cast<const Frag16*>(W);
   a.KT = K / Mfma16<T>::KF;
   a.n_tiles = N / 16;
@@ -566,14 +578,28 @@ dllm_status eval_block(dllm_ctx* c, const dllm_canvas* cv, const dllm_decode_cfg
   f.head_blk = B;
   f.head_off = s - f.row_start;
   TRY(forward<T>(c, f));
-  EpiLMHead eh{HR, B, d->gen_len, s - d->prompt_len, cv->bias_target, cv->bias_alpha, m.mask_id, m.vocab,
-               c->n_vtiles, c->pmax, c->psum, c->parg, dbg_logits};
+  // more block rows than one skinny launch covers: the LM head runs on the
+  // still-masked rows only (the large-M kernel skips row tiles past their
+  // count); up to 64 rows it streams the head weights once either way
+  const bool compact = HR > 64 && HR <= 32 * 1024;
+  const int* rowmap = compact ? c->head_rowmap : nullptr;
+  const int* count = compact ? c->head_count : nullptr;
   hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, c->stream, c->d_err, 2, 0);
+  if (compact) {
+    hipLaunchKernelGGL(head_rows_kernel, dim3(1), dim3(1024), 0, c->stream, cv->tokens, f.seq_len, s, B, HR,
+                       m.mask_id, c->head_rowmap, c->head_count);
+    hipLaunchKernelGGL(head_gather_kernel, dim3(HR), dim3(256), 0, c->stream, static_cast<const Frag16*>(c->xh),
+                       c->ssq_head, HR, m.d_model / Mfma16<T>::KF, m.d_model / 16, c->head_rowmap, c->head_count,
+                       static_cast<Frag16*>(c->xc), c->ssq_c);
+  }
   TRY(check_launch());
-  TRY(launch_gemm<T>(c, DLLM_K_LMHEAD, c->xh, c->wlm, HR, m.vocab, m.d_model, eh, c->ssq_head, HR));
+  EpiLMHead eh{HR, B, d->gen_len, s - d->prompt_len, cv->bias_target, cv->bias_alpha, m.mask_id, m.vocab,
+               c->n_vtiles, c->pmax, c->psum, c->parg, dbg_logits, rowmap, count};
+  TRY(launch_gemm<T>(c, DLLM_K_LMHEAD, compact ? c->xc : c->xh, c->wlm, HR, m.vocab, m.d_model, eh,
+                     compact ? c->ssq_c : c->ssq_head, HR, count));
   Timed tm(c, DLLM_K_MERGE, 12.0 * c->n_vtiles * HR + 8.0 * HR, 3.0 * c->n_vtiles * HR);
   hipLaunchKernelGGL(lm_merge_kernel, dim3(HR), dim3(kMergeThreads), 0, c->stream, c->pmax, c->psum, c->parg, c->n_vtiles,
-                     HR, c->conf, c->tok, c->d_err);
+                     HR, c->conf, c->tok, c->d_err, rowmap, count);
   return tm.done();
 }
 
@@ -775,6 +801,10 @@ dllm_status init_impl(dllm_ctx* c, const void* const* t) {
   TRY(c->alloc(&c->xh, (size_t)c->max_head_pad * d * es));
   TRY(c->alloc(&c->ssq, (size_t)(d / 16) * c->max_rows * sizeof(float)));
   TRY(c->alloc(&c->ssq_head, (size_t)(d / 16) * c->max_head * sizeof(float)));
+  TRY(c->alloc(&c->head_rowmap, (size_t)c->max_head * sizeof(int)));
+  TRY(c->alloc(&c->head_count, sizeof(int)));
+  TRY(c->alloc(&c->xc, (size_t)c->max_head_pad * d * es));
+  TRY(c->alloc(&c->ssq_c, (size_t)(d / 16) * c->max_head * sizeof(float)));
   c->rstd_rows = std::max(c->max_rows, c->max_head);
   TRY(c->alloc(&c->rstd, (size_t)c->rstd_rows * sizeof(float)));
   c->n_vtiles = V / 16;

@@ -183,14 +183,19 @@ struct EpiLMHead {
   float* pmax;            // [M][n_tiles]: each row's partials contiguous for the merge
   float* psum;
   int* parg;
-  float* dbg;             // [M][vocab] or null
+  float* dbg;             // [M][vocab] (block rows) or null
+  // optional compaction: partial row m is block row rowmap[m], rows >= *count
+  // are not written
+  const int* rowmap;
+  const int* count;
   __device__ void operator()(int nt, int mt, const f32x4& acc, int lane) const {
     const int m = mt * 16 + (lane & 15);
-    const bool valid = m < M;
+    const bool valid = m < (count ? *count : M);
+    const int br = rowmap ? rowmap[valid ? m : 0] : m;   // block row
     int tgt = -1;
     float al = 0.f;
     if (valid && target) {
-      const int bi = (m / blk) * gen_len + gen_off + m % blk;
+      const int bi = (br / blk) * gen_len + gen_off + br % blk;
       tgt = target[bi];
       al = alpha[bi];
     }
@@ -205,7 +210,7 @@ struct EpiLMHead {
       if (voc == mask_id) x = -INFINITY;
       v[r] = x;
       if (x > mx) { mx = x; am = voc; }
-      if (valid && dbg) dbg[(size_t)m * vocab + voc] = x;
+      if (valid && dbg) dbg[(size_t)br * vocab + voc] = x;
     }
 #pragma unroll
     for (int o = 16; o <= 32; o <<= 1) {
@@ -249,6 +254,9 @@ struct GemmArgs {
   // epilogue.
   int k_splits;
   float* part;
+  // gemm_big_kernel: when set, only rows < *m_count are needed; workgroups
+  // whose rows all lie beyond it return at once
+  const int* m_count;
 };
 
 // Workgroup i runs on XCD i % 8; map consecutive logical ids to one XCD so the
@@ -473,6 +481,7 @@ __global__ __launch_bounds__(64 * WN * WM) void gemm_big_kernel(GemmArgs a, Epi 
   const int split = lin_all / per_split, lin = lin_all % per_split;
   const int wg_m = lin % m_wg, wg_n = lin / m_wg;   // m fastest: neighbours share the weight tile
   const int nt0 = wg_n * NTW, mt0 = wg_m * MTW;
+  if (a.m_count && mt0 * 16 >= *a.m_count) return;
   const int wn = wave % WN, wm = wave / WN;
   const int nst_all = a.KT / KS;
   const int st_first = (int)((long)nst_all * split / k_splits);

@@ -66,15 +66,20 @@ __device__ __forceinline__ void argmax_take(float& mx, int& am, float v, int a) 
   if (v > mx || (v == mx && a < am)) { mx = v; am = a; }
 }
 
+// rowmap/count (optional, see head_rows_kernel): partial row m belongs to block
+// row rowmap[m]; rows m >= count are skipped.
 __global__ __launch_bounds__(kMergeThreads) void lm_merge_kernel(const float* pmax, const float* psum,
                                                                  const int* parg, int n_tiles, int M,
-                                                                 float* conf, int* tok, int* err) {
+                                                                 float* conf, int* tok, int* err,
+                                                                 const int* rowmap, const int* count) {
   (void)M;
   constexpr int NWV = kMergeThreads / 64;
   __shared__ float shm[NWV];
   __shared__ int sha[NWV];
   __shared__ float shs[NWV];
   const int m = blockIdx.x, t0 = threadIdx.x, lane = t0 & 63, wv = t0 >> 6;
+  if (count && m >= *count) return;
+  const int out_row = rowmap ? rowmap[m] : m;
   const float* rmax = pmax + (size_t)m * n_tiles;
   const float* rsum = psum + (size_t)m * n_tiles;
   const int* rarg = parg + (size_t)m * n_tiles;
@@ -108,10 +113,61 @@ __global__ __launch_bounds__(kMergeThreads) void lm_merge_kernel(const float* pm
   for (int t = t0 + kMergePer * kMergeThreads; t < n_tiles; t += kMergeThreads) s += rsum[t] * expf(rmax[t] - gm);
   s = block_sum<kMergeThreads>(s, shs);
   if (t0 == 0) {
-    conf[m] = 1.0f / s;
-    tok[m] = ga;
+    conf[out_row] = 1.0f / s;
+    tok[out_row] = ga;
     if (!(fabsf(gm) <= 3.0e38f) || !(s >= 1.0f && s <= 3.0e38f)) atomicOr(err, 1);
   }
+}
+
+// ---- LM head over the still-masked rows ------------------------------------
+// With more block rows than one skinny launch covers, the LM head runs only on
+// the rows whose canvas position still holds MASK (committed rows take no part
+// in the selection).  rowmap[k] = the k-th such block row b * blk + i, in row
+// order; count[0] = their number.  One workgroup of 1024 threads, each owning
+// `per` consecutive rows (rows <= 32 * 1024).
+__global__ __launch_bounds__(1024) void head_rows_kernel(const int* tokens, int seq_len, int start, int blk,
+                                                         int rows, int mask_id, int* rowmap, int* count) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  const int per = (rows + 1023) / 1024;
+  unsigned flags = 0;
+  int n = 0;
+  for (int u = 0; u < per; ++u) {
+    const int r = t * per + u;
+    const bool msk = r < rows && tokens[(size_t)(r / blk) * seq_len + start + r % blk] == mask_id;
+    flags |= (msk ? 1u : 0u) << u;
+    n += msk ? 1 : 0;
+  }
+  part[t] = n;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {   // inclusive scan of the per-thread counts
+    const int v = t >= o ? part[t - o] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int k = part[t] - n;
+  for (int u = 0; u < per; ++u)
+    if ((flags >> u) & 1u) rowmap[k++] = t * per + u;
+  if (t == 1023) count[0] = part[1023];
+}
+
+// Packed row k of xc = packed row rowmap[k] of xh (in every k-fragment, row i
+// of a 16-row tile is lanes i + 16 g, g < 4), and the row's sum-of-squares
+// partials: ssq_c[t][k] = ssq[t][rowmap[k]] (both [tiles][ld]).
+__global__ __launch_bounds__(256) void head_gather_kernel(const Frag16* xh, const float* ssq, int ld, int KT,
+                                                          int ssq_tiles, const int* rowmap, const int* count,
+                                                          Frag16* xc, float* ssq_c) {
+  const int k = blockIdx.x;
+  if (k >= *count) return;
+  const int r = rowmap[k];
+  const Frag16* src = xh + (size_t)(r >> 4) * KT * 64 + (r & 15);
+  Frag16* dst = xc + (size_t)(k >> 4) * KT * 64 + (k & 15);
+  for (int c = threadIdx.x; c < KT * 4; c += 256) {
+    const size_t o = (size_t)(c >> 2) * 64 + 16 * (c & 3);
+    dst[o] = src[o];
+  }
+  for (int t = threadIdx.x; t < ssq_tiles; t += 256) ssq_c[(size_t)t * ld + k] = ssq[(size_t)t * ld + r];
 }
 
 // ---- select / commit: one workgroup per sequence ---------------------------
