@@ -39,17 +39,47 @@ __global__ __launch_bounds__(256) void embed_kernel(const int* tokens, int seq_l
   const int b = m / g.nr, pos = g.row_start + m % g.nr;
   const int tok = min(max(tokens[(size_t)b * seq_len + pos], 0), vocab - 1);
   const Tin* e = emb + (size_t)tok * d;
-  for (int t = threadIdx.x; t < d / 16; t += 256) {
-    float s = 0.f;
+  if constexpr (sizeof(Tin) == 2 && sizeof(T) == 2) {
+    // 16 consecutive columns per thread with 16-byte accesses: the packed
+    // input holds columns 8j .. 8j+7 of a row in one 16-byte slot group
+    for (int t = threadIdx.x; t < d / 16; t += 256) {
+      Tin ev[16];
+      *reinterpret_cast<uint4*>(ev) = reinterpret_cast<const uint4*>(e + t * 16)[0];
+      *reinterpret_cast<uint4*>(ev + 8) = reinterpret_cast<const uint4*>(e + t * 16)[1];
+      float v[16], gv[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int k = t * 16 + u;
-      const float v = Elem<Tin>::load(e + k);
-      x[(size_t)m * d + k] = v;
-      xg[packed_off<T>(m, k, d)] = Elem<T>::cvt(v * gain[k]);
-      s += v * v;
+      for (int q = 0; q < 4; ++q) *reinterpret_cast<float4*>(gv + 4 * q) = reinterpret_cast<const float4*>(gain + t * 16)[q];
+      float s = 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        v[u] = Elem<Tin>::load(ev + u);
+        s += v[u] * v[u];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        reinterpret_cast<float4*>(x + (size_t)m * d + t * 16)[q] = float4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        T o[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o[u] = Elem<T>::cvt(v[8 * h + u] * gv[8 * h + u]);
+        *reinterpret_cast<uint4*>(xg + packed_off<T>(m, t * 16 + 8 * h, d)) = *reinterpret_cast<const uint4*>(o);
+      }
+      ssq[(size_t)t * g.M + m] = s;
     }
-    ssq[(size_t)t * g.M + m] = s;
+  } else {
+    for (int t = threadIdx.x; t < d / 16; t += 256) {
+      float s = 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int k = t * 16 + u;
+        const float v = Elem<Tin>::load(e + k);
+        x[(size_t)m * d + k] = v;
+        xg[packed_off<T>(m, k, d)] = Elem<T>::cvt(v * gain[k]);
+        s += v * v;
+      }
+      ssq[(size_t)t * g.M + m] = s;
+    }
   }
 }
 
