@@ -304,24 +304,26 @@ dllm_status launch_skinny_nt(dllm_ctx* c, const Timed& tm, const GemmArgs& a, co
   return launch_skinny<T, MT, 1, 4>(c, tm, a, epi);
 }
 
-// Large-M tile shapes (NTW x MTW 16x16 tiles per workgroup), measured on
-// MI355X for the LLaDA-8B cache-pass, batch-16 and block-diffusion shapes;
-// eff is the relative throughput of one busy CU.  192 columns x 256 rows
-// fills one round exactly at 512 rows (gate/up: 147 -> 96 us) and four
-// rounds at 2048.
-struct BigCfg { int ntw, mtw; double eff; };
-constexpr BigCfg kBigCfgs[] = {{12, 12, 1.0}, {16, 8, 0.85}, {8, 8, 0.75}, {8, 6, 0.72}, {12, 16, 1.05}};
+// Large-M tile shapes (NTW x MTW 16x16 tiles per workgroup) and their cost
+// on one CU, fitted to MI355X sweeps of the LLaDA-8B projections (Q/K/V, O,
+// gate/up and down at 128-4096 rows, each with its real epilogue): a round of
+// up to 256 workgroups takes f0_us + step_ns per k-fragment (32 of K at
+// 16 bits).
+// 192 columns x 256 rows fills one round exactly at 512 rows (gate/up) and
+// four at 2048; 192 x 128 does the same for the Q/K/V projection at 512 rows
+// (92 -> 73 us); 128 x 64 serves short O and down projections at 128-512 rows.
+struct BigCfg { int ntw, mtw; double f0_us, step_ns; };
+constexpr BigCfg kBigCfgs[] = {{12, 12, 14.5, 521.0}, {16, 8, 11.5, 506.0}, {8, 8, 2.3, 357.0}, {8, 6, 2.4, 280.0},
+                               {12, 16, 25.5, 562.0}, {12, 8, 7.2, 423.0}, {8, 4, 2.0, 236.0}};
 constexpr int kNumBigCfgs = sizeof(kBigCfgs) / sizeof(kBigCfgs[0]);
 
 // K splits of a large-M projection: when the best tile leaves most CUs
 // idle (few output tiles, long K: the down and O projections at 128-512
 // rows), the K range is split over 2-4 workgroups per tile whose fp32 partial
 // tiles are added, in split order, by gemm_split_reduce_kernel, which also
-// runs the epilogue.  Estimated time (us, fitted to MI355X sweeps of the
-// LLaDA-8B shapes): rounds of 256 workgroups x tile area x k-fragments per
-// split x 4.3 ns / eff, plus for splits the partial tiles written and read
-// back at ~6 TB/s (they largely stay in the memory-side cache) and one more
-// launch.
+// runs the epilogue.  The split costs the partial tiles' round trip and the
+// second launch: about 4.6 us per million outputs, at least 3 us (same
+// sweeps).
 constexpr int kMaxKSplits = 4;
 constexpr int kMinStagesPerSplit = 16;
 // The Q/K/V epilogue (rotary, scattered cache writes) costs the reduce kernel
@@ -334,6 +336,7 @@ template <typename T, class Epi>
 dllm_status launch_big(dllm_ctx* c, GemmArgs a, const Epi& epi) {
   int best = 0, best_s = 1;
   double best_t = 1e300;
+  const double outputs = 256.0 * a.m_tiles * a.n_tiles;
   for (int i = 0; i < kNumBigCfgs; ++i) {
     const BigCfg& g = kBigCfgs[i];
     const double nwg = (double)cdiv(a.n_tiles, g.ntw) * cdiv(a.m_tiles, g.mtw);
@@ -341,9 +344,8 @@ dllm_status launch_big(dllm_ctx* c, GemmArgs a, const Epi& epi) {
       if (sp > 1 && (!kSplitOk<Epi> || a.KT / 2 < sp * kMinStagesPerSplit ||
                      (size_t)sp * a.m_tiles * a.n_tiles * 256 > c->gemm_part_floats))
         break;
-      const double part_bytes = sp > 1 ? 8.0 * sp * a.m_tiles * 16.0 * a.n_tiles * 16.0 : 0.0;
-      const double t = std::ceil(nwg * sp / 256.0) * g.ntw * g.mtw * ((double)a.KT / sp) * 4.3e-3 / g.eff +
-                       (sp > 1 ? part_bytes / 6.0e6 + 3.0 : 0.0);
+      const double t = std::ceil(nwg * sp / 256.0) * (g.f0_us + g.step_ns * 1e-3 * ((double)a.KT / sp)) +
+                       (sp > 1 ? std::max(3.0, 4.6e-6 * outputs - 5.3) : 0.0);
       if (t < best_t) { best_t = t; best = i; best_s = sp; }
     }
   }
@@ -359,6 +361,8 @@ dllm_status launch_big(dllm_ctx* c, GemmArgs a, const Epi& epi) {
     case 2: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 8, 2, 2, 2, 4>), grid(8, 8), dim3(256), 0, c->stream, a, epi); break;
     case 3: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 6, 2, 2, 2, 5>), grid(8, 6), dim3(256), 0, c->stream, a, epi); break;
     case 4: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 12, 16, 2, 4, 2, 2>), grid(12, 16), dim3(512), 0, c->stream, a, epi); break;
+    case 5: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 12, 8, 4, 2, 2, 3>), grid(12, 8), dim3(512), 0, c->stream, a, epi); break;
+    case 6: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 4, 2, 2, 2, 6>), grid(8, 4), dim3(256), 0, c->stream, a, epi); break;
     default: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 8, 2, 2, 1, 6>), grid(8, 8), dim3(256), 0, c->stream, a, epi); break;
   }
   if (best_s > 1)
