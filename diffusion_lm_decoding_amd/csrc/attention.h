@@ -75,12 +75,14 @@ struct AttnWork {
   int m, limit;   // this lane's query row and its key limit
   bool valid;
   int t0, t1;     // key tiles [t0, t1) of this share
-  __device__ AttnWork(const AttnArgs& a) {
+  // key share split_ of splits_ (blockIdx.y of a.splits by default)
+  __device__ AttnWork(const AttnArgs& a) : AttnWork(a, blockIdx.y, a.splits) {}
+  __device__ AttnWork(const AttnArgs& a, int split_, int splits_) {
     lane = threadIdx.x & 63;
     wave = threadIdx.x >> 6;
     hf = lane >> 5;
     wg = blockIdx.x;
-    split = blockIdx.y;
+    split = split_;
     const int qb = wg % a.qblocks, bh = wg / a.qblocks;
     h = bh % a.H;
     b = bh / a.H;
@@ -90,19 +92,19 @@ struct AttnWork {
     limit = valid ? attn_limit(a, a.g.row_start + irow) : 0;
     const int last = min(a.g.nr, qb * 32 + 32) - 1;
     const int ntile = (attn_limit(a, a.g.row_start + last) + 31) / 32;
-    t0 = (int)((long)ntile * split / a.splits);
-    t1 = (int)((long)ntile * (split + 1) / a.splits);
+    t0 = (int)((long)ntile * split / splits_);
+    t1 = (int)((long)ntile * (split + 1) / splits_);
   }
 };
 
-// S^T = K Q^T for one 32-key tile, online-softmax update, o += P V.
-// kf: K fragments of the tile; for 16-bit types vf holds the V^T fragments
-// (d-tile i, key half c) in vt_col order.
-template <typename T, int DH>
+// S^T = K Q^T for one 32-key tile, online-softmax update, o += P V over ND
+// 32-dim output tiles.  kf: K fragments of the tile; for 16-bit types vf holds
+// the V^T fragments (d-tile i, key half c) in vt_col order.
+template <typename T, int DH, int ND = DH / 32>
 __device__ __forceinline__ void attn_tile16(const Frag16 (&qf)[DH / 16], const Frag16 (&kf)[DH / 16],
-                                            const Frag16 (&vf)[DH / 32][2], int kb, int limit, float scale_log2,
-                                            float& mrun, float& lrun, f32x16 (&o)[DH / 32], int lane) {
-  constexpr int NQF = DH / 16, ND = DH / 32;
+                                            const Frag16 (&vf)[ND][2], int kb, int limit, float scale_log2,
+                                            float& mrun, float& lrun, f32x16 (&o)[ND], int lane) {
+  constexpr int NQF = DH / 16;
   f32x16 s;
 #pragma unroll
   for (int r = 0; r < 16; ++r) s[r] = 0.f;
@@ -145,12 +147,12 @@ __device__ __forceinline__ void attn_tile16(const Frag16 (&qf)[DH / 16], const F
 }
 
 // Merge the NW wave states (tree in LDS, lds: >= (NW/2) * (2 + 16 ND) * 64
-// floats, free on entry), then wave 0 writes the normalised output or, with
-// several key shares, the share's state to the workspace.
-template <typename T, int DH, int NW>
+// floats, free on entry), then wave 0 writes the normalised output dims
+// [d0, d0 + 32 ND) of the head or, with several key shares (ND = DH/32), the
+// share's state to the workspace.
+template <typename T, int DH, int NW, int ND = DH / 32>
 __device__ __forceinline__ void attn_finish(const AttnArgs& a, const AttnWork& w, float mrun, float lrun,
-                                            f32x16 (&o)[DH / 32], float* lds) {
-  constexpr int ND = DH / 32;
+                                            f32x16 (&o)[ND], float* lds, int d0 = 0) {
   const int lane = w.lane, wave = w.wave;
   if constexpr (NW > 1) {
     float (*sm_m)[64] = reinterpret_cast<float (*)[64]>(lds);
@@ -191,11 +193,11 @@ __device__ __forceinline__ void attn_finish(const AttnArgs& a, const AttnWork& w
   for (int i = 0; i < ND; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      out[packed_off<T>(w.m, w.h * DH + i * 32 + acc32_row(r, lane), a.d)] = Elem<T>::cvt(o[i][r] * inv);
+      out[packed_off<T>(w.m, w.h * DH + d0 + i * 32 + acc32_row(r, lane), a.d)] = Elem<T>::cvt(o[i][r] * inv);
 }
 
-template <int NW, int DH>
-constexpr int attn_merge_floats() { return (NW / 2) * (2 + 16 * (DH / 32)) * 64; }
+template <int NW, int DH, int ND = DH / 32>
+constexpr int attn_merge_floats() { return (NW / 2) * (2 + 16 * ND) * 64; }
 
 // Fragments are loaded into registers per tile: with the key shares spread
 // over all CUs each wave holds about one tile, so a deeper copy pipeline has
@@ -297,6 +299,61 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
     }
   }
   attn_finish<T, DH, NW>(a, w, mrun, lrun, o, lds);
+}
+
+// Few (sequence, head, 32-query) blocks (block steps of small batches;
+// 16-bit caches): instead of key shares combined by a second launch, grid.y
+// cuts the head's output dims into DH / (32 ND) slices.  Each workgroup runs
+// the online softmax over every key tile (the scores are recomputed per
+// slice: 8 MFMAs a tile, little next to the loads) and accumulates P V for
+// its ND 32-dim output tiles only, so it writes final outputs and no merge
+// kernel follows.  Its NW waves take the key tiles round-robin, requesting
+// the next tile's fragments before the current tile's math, and are merged
+// by the LDS tree.
+template <typename T, int DH, int NW, int ND>
+__global__ __launch_bounds__(64 * NW) void attn_dslice_kernel(AttnArgs a) {
+  static_assert(sizeof(T) == 2, "16-bit caches");
+  constexpr int NQF = DH / 16;
+  __shared__ float lds[attn_merge_floats<NW, DH, ND>() > 0 ? attn_merge_floats<NW, DH, ND>() : 1];
+  const AttnWork w(a, 0, 1);
+  const int lane = w.lane, hf = w.hf;
+  const int d0 = blockIdx.y * ND * 32;
+  const T* q = static_cast<const T*>(a.q);
+  const T* kc = static_cast<const T*>(a.kc) + ((size_t)w.b * a.H + w.h) * a.seq_pad * DH;
+  const T* vt = static_cast<const T*>(a.vt) + ((size_t)w.b * a.H + w.h) * DH * a.seq_pad + (size_t)d0 * a.seq_pad;
+  Frag16 qf[NQF];
+#pragma unroll
+  for (int c = 0; c < NQF; ++c) qf[c] = *reinterpret_cast<const Frag16*>(q + (size_t)w.m * a.d + w.h * DH + c * 16 + 8 * hf);
+  float mrun = -INFINITY, lrun = 0.f;
+  f32x16 o[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
+  auto load = [&](int t, Frag16 (&kf)[NQF], Frag16 (&vf)[ND][2]) {
+    const int kb = t * 32;
+    const T* krow = kc + (size_t)(kb + (lane & 31)) * DH;
+#pragma unroll
+    for (int c = 0; c < NQF; ++c) kf[c] = *reinterpret_cast<const Frag16*>(krow + c * 16 + 8 * hf);
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        vf[i][c] = *reinterpret_cast<const Frag16*>(vt + (size_t)(i * 32 + (lane & 31)) * a.seq_pad + kb + (2 * c + hf) * 8);
+  };
+  Frag16 ka[NQF], va[ND][2], kb2[NQF], vb[ND][2];
+  int t = w.t0 + w.wave;
+  if (t < w.t1) load(t, ka, va);
+  for (; t < w.t1; t += 2 * NW) {
+    const bool second = t + NW < w.t1;
+    if (second) load(t + NW, kb2, vb);
+    attn_tile16<T, DH, ND>(qf, ka, va, t * 32, w.limit, a.scale_log2, mrun, lrun, o, lane);
+    if (second) {
+      if (t + 2 * NW < w.t1) load(t + 2 * NW, ka, va);
+      attn_tile16<T, DH, ND>(qf, kb2, vb, (t + NW) * 32, w.limit, a.scale_log2, mrun, lrun, o, lane);
+    }
+  }
+  attn_finish<T, DH, NW, ND>(a, w, mrun, lrun, o, lds, d0);
 }
 
 // Many query rows (cache passes, block-diffusion steps; 16-bit caches): a

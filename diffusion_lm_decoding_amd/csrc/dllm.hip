@@ -281,9 +281,9 @@ dllm_status launch_skinny(dllm_ctx* c, const Timed& tm, const GemmArgs& a, const
 
 // n-tiles per workgroup: exactly one round of 256 workgroups when N/16 is 256,
 // 512, 768 or 1024 (measured best on MI355X for the LLaDA-8B shapes: every CU
-// streams one contiguous weight slice); otherwise the largest NT whose grid
-// is one partial round (192..256 workgroups) or whole rounds of 256; very
-// wide outputs take NT = 2.
+// streams one contiguous weight slice), two rounds of 3 at 1536; otherwise
+// the largest NT whose grid is one partial round (192..256 workgroups) or
+// whole rounds of 256; very wide outputs take NT = 2.
 template <typename T, int MT, class Epi>
 dllm_status launch_skinny_nt(dllm_ctx* c, const Timed& tm, const GemmArgs& a, const Epi& epi) {
   auto fits = [&](int nt) {
@@ -293,7 +293,8 @@ dllm_status launch_skinny_nt(dllm_ctx* c, const Timed& tm, const GemmArgs& a, co
   };
   // U (fragments per pipelined batch) keeps both register sets in VGPRs
   if constexpr (MT <= 2) {
-    if (a.n_tiles == 3 * 256) return launch_skinny<T, MT, 3, 2>(c, tm, a, epi);
+    // N/16 = 1536 (gate/up): two rounds of 3 n-tiles, 37.5 -> 35.6 us
+    if (a.n_tiles == 3 * 256 || a.n_tiles == 6 * 256) return launch_skinny<T, MT, 3, 2>(c, tm, a, epi);
     if (a.n_tiles == 4 * 256 || (a.n_tiles != 2 * 256 && fits(4))) return launch_skinny<T, MT, 4, 2>(c, tm, a, epi);
   }
   if (fits(2) || (a.n_tiles % 2 == 0 && a.n_tiles / 2 >= 2048))
@@ -474,6 +475,21 @@ dllm_status launch_attn(dllm_ctx* c, int layer, const Fwd& f) {
         const int g2 = f.batch * m.n_heads * cdiv(a.qblocks, 2);
         hipLaunchKernelGGL((attn_wide_kernel<T, DH, 2, 4>), dim3(g2), dim3(128), 0, c->stream, a);
       }
+      return tm.done();
+    }
+  }
+  if constexpr (sizeof(T) == 2 && DH % 64 == 0) {
+    // two key shares: output-dim slices, which need no merge launch, are
+    // faster (measured on MI355X at 32-query blocks: 256 keys 10.9 -> 7.5 us
+    // at batch 1, 12.4 -> 9.5 us at batch 4; 768 keys 18.6 -> 15.6 us at
+    // batch 4).  With more shares (longer keys, fewer blocks) every slice
+    // rereads all keys and the shares win.
+    if (splits == 2) {
+      a.splits = 1;
+      if (nwg * (DH / 32) <= 256)
+        hipLaunchKernelGGL((attn_dslice_kernel<T, DH, 4, 1>), dim3(nwg, DH / 32), dim3(256), 0, c->stream, a);
+      else
+        hipLaunchKernelGGL((attn_dslice_kernel<T, DH, 4, 2>), dim3(nwg, DH / 64), dim3(256), 0, c->stream, a);
       return tm.done();
     }
   }
