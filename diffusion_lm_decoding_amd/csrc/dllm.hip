@@ -283,7 +283,7 @@ dllm_status launch_skinny(dllm_ctx* c, const Timed& tm, const GemmArgs& a, const
 // 512, 768 or 1024 (measured best on MI355X for the LLaDA-8B shapes: every CU
 // streams one contiguous weight slice), two rounds of 3 at 1536; otherwise
 // the largest NT whose grid is one partial round (192..256 workgroups) or
-// whole rounds of 256; very wide outputs take NT = 2.
+// whole rounds of 256; very wide outputs take NT = 4 (up to 32 rows) or 2.
 template <typename T, int MT, class Epi>
 dllm_status launch_skinny_nt(dllm_ctx* c, const Timed& tm, const GemmArgs& a, const Epi& epi) {
   auto fits = [&](int nt) {
@@ -296,6 +296,9 @@ dllm_status launch_skinny_nt(dllm_ctx* c, const Timed& tm, const GemmArgs& a, co
     // N/16 = 1536 (gate/up): two rounds of 3 n-tiles, 37.5 -> 35.6 us
     if (a.n_tiles == 3 * 256 || a.n_tiles == 6 * 256) return launch_skinny<T, MT, 3, 2>(c, tm, a, epi);
     if (a.n_tiles == 4 * 256 || (a.n_tiles != 2 * 256 && fits(4))) return launch_skinny<T, MT, 4, 2>(c, tm, a, epi);
+    // very wide outputs (the LM head): 4 n-tiles in batches of one fragment
+    // (126464 x 4096 head at 32 rows: 172-187 -> 158 us)
+    if (a.n_tiles % 4 == 0 && a.n_tiles >= 4096) return launch_skinny<T, MT, 4, 1>(c, tm, a, epi);
   }
   if (fits(2) || (a.n_tiles % 2 == 0 && a.n_tiles / 2 >= 2048))
     return launch_skinny<T, MT, 2, (MT <= 2 ? 4 : 2)>(c, tm, a, epi);

@@ -24,6 +24,22 @@ struct RowGeom {
   int row_start;  // canvas position of each sequence's first row
 };
 
+// N consecutive 16-bit elements (N = 2 or 4, p aligned to 2N bytes) as one
+// store; fp32 elements one by one.  Rounding as Elem<T>::cvt.
+template <typename T, int N>
+__device__ __forceinline__ void store_run(T* p, const float (&v)[N]) {
+  if constexpr (sizeof(T) == 2) {
+    uint32_t w[N / 2];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) w[i] = Elem<T>::bits(v[2 * i]) | (Elem<T>::bits(v[2 * i + 1]) << 16);
+    if constexpr (N == 4) *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+    else *reinterpret_cast<uint32_t*>(p) = w[0];
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) p[i] = Elem<T>::cvt(v[i]);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // epilogues: called once per (16-col n-tile, 16-row m-tile); lane l holds
 // rows n = 16*nt + 4*(l/16) + r (r = 0..3) of token m = 16*mt + l%16.
@@ -75,8 +91,7 @@ struct EpiQKV {
         v[t + 1] = o * c + e * s;
       }
       T* dst = region == 0 ? q + (size_t)m * d + nn : kc + (((size_t)b * H + h) * seq_pad + pos) * dh + p;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) dst[t] = Elem<T>::cvt(v[t]);
+      store_run<T, 4>(dst, v);
     } else {
 #pragma unroll
       for (int t = 0; t < 4; ++t) vt[(((size_t)b * H + h) * dh + p + t) * seq_pad + vt_col<T>(pos)] = Elem<T>::cvt(v[t]);
@@ -106,8 +121,14 @@ struct NormOut {
     s += __shfl_xor(s, 16);
     s += __shfl_xor(s, 32);
     if (!keep) return;
+    if constexpr (sizeof(T) == 2) {
+      // 16-bit packing keeps k = n0..n0+3 (n0 % 4 == 0) in adjacent slots
+      const float w[4] = {v[0] * gain[n0], v[1] * gain[n0 + 1], v[2] * gain[n0 + 2], v[3] * gain[n0 + 3]};
+      store_run<T, 4>(xg + packed_off<T>(mo, n0, d), w);
+    } else {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) xg[packed_off<T>(mo, n0 + t, d)] = Elem<T>::cvt(v[t] * gain[n0 + t]);
+      for (int t = 0; t < 4; ++t) xg[packed_off<T>(mo, n0 + t, d)] = Elem<T>::cvt(v[t] * gain[n0 + t]);
+    }
     if (lane < 16) ssq[(size_t)nt * rows_out + mo] = s;
   }
 };
@@ -159,11 +180,18 @@ struct EpiSwiGLU {
     const int m = mt * 16 + (lane & 15);
     if (m >= M) return;
     const int i0 = (nt * 16 + 4 * (lane >> 4)) >> 1;
+    float h[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const float gt = acc[2 * t], up = acc[2 * t + 1];
       const float s = gt / (1.0f + expf(-gt));
-      a[packed_off<T>(m, i0 + t, F)] = Elem<T>::cvt(s * up);
+      h[t] = s * up;
+    }
+    if constexpr (sizeof(T) == 2) {
+      store_run<T, 2>(a + packed_off<T>(m, i0, F), h);  // i0 even: adjacent slots
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) a[packed_off<T>(m, i0 + t, F)] = h[t];
     }
   }
 };

@@ -215,10 +215,11 @@ def test_fixed_count_rules_lockstep(big, k):
            f"top-{k}")
 
 
-@pytest.mark.parametrize("batch", [4, 8])
-def test_batch_4_and_8_first_step(big, batch):
-    """Batch shapes between 1 and 16 (P 128, L 128, B 32): the step has
-    batch x 32 rows; the first and last sequences are checked."""
+@pytest.mark.parametrize("batch", [1, 2, 4, 8])
+def test_batch_1_to_8_first_step(big, batch):
+    """Batch shapes below 16 (P 128, L 128, B 32): the step has batch x 32
+    rows; the first and last sequences are checked.  Batches 1 and 2 run the
+    attention as output-dim slices of one 32-dim tile, batch 4 of two."""
     from diffusion_lm_decoding_amd.engine import Engine
     eng, om = big
     w = workload("llada8b_p128_g128", alpha_max=24.0)
@@ -232,7 +233,7 @@ def test_batch_4_and_8_first_step(big, batch):
     after = cv.tokens.cpu().numpy()
     rep = Report()
     dec = OracleDecoder(om, 128, 128, 32, cache="dual")
-    for b in (0, batch - 1):
+    for b in sorted({0, batch - 1}):
         st = dec.new_state(pr[b], t[b], a[b])
         st.canvas[:] = before[b]
         dec.refresh(st)
