@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--batch", type=int, default=0, help="override the workload batch")
     p.add_argument("--cache", default="", help="override the cache mode")
     p.add_argument("--rule", default="", help="override the rule")
+    p.add_argument("--factor", type=float, default=0.0, help="override the factor-rule f")
+    p.add_argument("--k", type=int, default=0, help="override the tokens per step of the top-k rule")
     p.add_argument("--cpu-steps", type=int, default=16, help="oracle denoising steps timed for cpu_baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-b16", action="store_true", help="skip the batch-16 projection MFMA-fraction measurement")
@@ -86,7 +88,8 @@ def main():
     from diffusion_lm_decoding_amd.engine import Engine
     from workloads import gen_bias, gen_prompt, gen_tensor, workload
 
-    over = {k: v for k, v in (("batch", args.batch), ("cache", args.cache), ("rule", args.rule)) if v}
+    over = {k: v for k, v in (("batch", args.batch), ("cache", args.cache), ("rule", args.rule),
+                              ("factor", args.factor), ("k", args.k)) if v}
     w = workload(args.workload, **over)
     shape = w.model
     dev = torch.device("cuda:0")
@@ -176,6 +179,8 @@ def main():
         "data": "synthetic (counter-hash random weights, uniform random prompt, planted logit bias)",
         "config": {"workload": w.name, "batch": w.batch, "prompt_len": w.prompt_len, "gen_len": w.gen_len,
                    "block_len": w.block_len, "cache": w.cache, "rule": w.rule, "tau": w.tau,
+                   **({"factor": w.factor} if w.rule == "factor" else {}),
+                   **({"k": w.k} if w.rule == "topk" else {}),
                    "alpha_max": w.alpha_max, "weights": shape.dtype},
         "denoise_steps_per_s": steps / elapsed,
         "tokens_per_denoise_step": committed / max(steps, 1),
