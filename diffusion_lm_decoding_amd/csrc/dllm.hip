@@ -300,6 +300,13 @@ dllm_status launch_skinny_nt(dllm_ctx* c, const Timed& tm, const GemmArgs& a, co
     // (126464 x 4096 head at 32 rows: 172-187 -> 158 us)
     if (a.n_tiles % 4 == 0 && a.n_tiles >= 4096) return launch_skinny<T, MT, 4, 1>(c, tm, a, epi);
   }
+  if constexpr (MT == 4) {
+    // 64 rows: 3 n-tiles in batches of one fragment for N/16 = 768 (Q/K/V
+    // 37 -> 24 us) and 1536 (gate/up 50-53 -> 45-49 us); 4 for the LM head,
+    // so each workgroup's reread of the rows stays below its weight bytes
+    if (a.n_tiles == 3 * 256 || a.n_tiles == 6 * 256) return launch_skinny<T, MT, 3, 1>(c, tm, a, epi);
+    if (a.n_tiles % 4 == 0 && a.n_tiles >= 4096) return launch_skinny<T, MT, 4, 1>(c, tm, a, epi);
+  }
   if (fits(2) || (a.n_tiles % 2 == 0 && a.n_tiles / 2 >= 2048))
     return launch_skinny<T, MT, 2, (MT <= 2 ? 4 : 2)>(c, tm, a, epi);
   // one n-tile: short K (the O projection) streams best in batches of 2
