@@ -161,6 +161,20 @@ def test_block_causal_lockstep(big):
                   max_steps=2), "block_causal")
 
 
+def test_block_causal_sliced_attention_lockstep(big):
+    """Block diffusion with blocks of 32 (batch 3, P 192, L 64, top-8 per
+    step): the block steps' 32 queries attend 224 or 256 keys, which runs the
+    output-dim-sliced attention (two slices per head at this batch) under the
+    block-causal key limit; the last sequence is followed."""
+    from diffusion_lm_decoding_amd.engine import Engine
+    eng, om = big
+    pr, t, a = _inputs(3, 192, 64, seed=2311, alpha_max=24.0)
+    cfg = Engine.decode_cfg(3, 192, 64, 32, cache="block_causal", rule="topk", k=8)
+    cv = eng.canvas(pr, t, a, 64)
+    _check(replay(eng, cv, cfg, om, pr, t, a, "block_causal", "topk", k=8, tol=Tol(fp32=False), seq=2,
+                  max_steps=8), "block_causal, sliced attention")
+
+
 def test_block_diffusion_full_size_first_step(big):
     """The block-diffusion workload at full size (batch 8, P 2048, L 1024,
     blocks of 256): the GPU's prompt pass over 8 x 2048 rows and first
