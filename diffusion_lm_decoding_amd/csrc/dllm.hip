@@ -322,10 +322,12 @@ dllm_status launch_skinny_nt(dllm_ctx* c, const Timed& tm, const GemmArgs& a, co
 // 16 bits).
 // 192 columns x 256 rows fills one round exactly at 512 rows (gate/up) and
 // four at 2048; 192 x 128 does the same for the Q/K/V projection at 512 rows
-// (92 -> 73 us); 128 x 64 serves short O and down projections at 128-512 rows.
+// (92 -> 73 us); 128 x 64 serves short O and down projections at 128-512 rows;
+// 96 x 128 fills one round for Q/K/V at 256 rows (56 -> 47 us) and gate/up at
+// 128 (46 -> 40 us).
 struct BigCfg { int ntw, mtw; double f0_us, step_ns; };
 constexpr BigCfg kBigCfgs[] = {{12, 12, 14.5, 521.0}, {16, 8, 11.5, 506.0}, {8, 8, 2.3, 357.0}, {8, 6, 2.4, 280.0},
-                               {12, 16, 25.5, 562.0}, {12, 8, 7.2, 423.0}, {8, 4, 2.0, 236.0}};
+                               {12, 16, 25.5, 562.0}, {12, 8, 7.2, 423.0}, {8, 4, 2.0, 236.0}, {6, 8, 2.0, 310.0}};
 constexpr int kNumBigCfgs = sizeof(kBigCfgs) / sizeof(kBigCfgs[0]);
 
 // K splits of a large-M projection: when the best tile leaves most CUs
@@ -374,6 +376,7 @@ dllm_status launch_big(dllm_ctx* c, GemmArgs a, const Epi& epi) {
     case 4: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 12, 16, 2, 4, 2, 2>), grid(12, 16), dim3(512), 0, c->stream, a, epi); break;
     case 5: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 12, 8, 4, 2, 2, 3>), grid(12, 8), dim3(512), 0, c->stream, a, epi); break;
     case 6: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 4, 2, 2, 2, 6>), grid(8, 4), dim3(256), 0, c->stream, a, epi); break;
+    case 7: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 6, 8, 2, 2, 2, 5>), grid(6, 8), dim3(256), 0, c->stream, a, epi); break;
     default: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 8, 2, 2, 1, 6>), grid(8, 8), dim3(256), 0, c->stream, a, epi); break;
   }
   if (best_s > 1)
