@@ -19,8 +19,8 @@ CACHE = {"none": 0, "prefix": 1, "dual": 2, "block_causal": 3}
 RULE = {"threshold": 0, "factor": 1, "topk": 2, "budget": 3, "steps": 4}
 
 SYMBOLS = ("dllm_init_weights", "dllm_refresh_cache", "dllm_block_step", "dllm_staleness", "dllm_begin_decode",
-           "dllm_decode", "dllm_set_timing", "dllm_get_timing", "dllm_probe_peaks", "dllm_destroy",
-           "dllm_last_error")
+           "dllm_decode", "dllm_set_timing", "dllm_get_timing", "dllm_probe_peaks", "dllm_set_device_limit",
+           "dllm_destroy", "dllm_last_error")
 KERNEL_CLASSES = ("embed", "rmsnorm", "qkv", "attn", "oproj", "gateup", "down", "lmhead", "merge",
                   "select")
 
@@ -51,7 +51,8 @@ class Canvas(C.Structure):
 
 class Stats(C.Structure):
     _fields_ = [("steps", C.c_int64), ("refreshes", C.c_int64), ("committed", C.c_int64),
-                ("max_seq_steps", C.c_int64), ("ms_total", C.c_double), ("ms_refresh", C.c_double)]
+                ("max_seq_steps", C.c_int64), ("ms_total", C.c_double), ("ms_refresh", C.c_double),
+                ("ms_step", C.c_double), ("ms_select", C.c_double)]
 
 
 class DllmError(RuntimeError):
@@ -91,6 +92,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.dllm_set_timing.restype = C.c_int
     lib.dllm_get_timing.argtypes = [P, C.POINTER(KernelTime), C.c_int32]
     lib.dllm_get_timing.restype = C.c_int
+    lib.dllm_set_device_limit.argtypes = [C.c_uint64]
+    lib.dllm_set_device_limit.restype = None
     lib.dllm_destroy.argtypes = [P]
     lib.dllm_destroy.restype = None
     lib.dllm_last_error.argtypes = []
@@ -164,6 +167,10 @@ def dllm_get_timing(ctx: int, reset: bool = True) -> dict:
         out[part] = {k: dict(launches=arr[off + i].launches, ms=arr[off + i].ms, bytes=arr[off + i].bytes,
                              flops=arr[off + i].flops) for i, k in enumerate(KERNEL_CLASSES)}
     return out
+
+
+def dllm_set_device_limit(nbytes: int) -> None:
+    load().dllm_set_device_limit(C.c_uint64(nbytes))
 
 
 def dllm_destroy(ctx: int) -> None:

@@ -5,6 +5,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <atomic>
 #include <chrono>
 #include <cmath>
 #include <cstdio>
@@ -23,6 +24,8 @@ using namespace dllm;
 namespace {
 
 thread_local std::string g_err;
+// dllm_set_device_limit: cap on the device bytes one context may hold (0: none)
+std::atomic<uint64_t> g_device_limit{0};
 
 dllm_status fail(dllm_status s, const std::string& msg) {
   g_err = msg;
@@ -67,6 +70,11 @@ struct dllm_ctx {
   int n_vtiles = 0;
 
   std::vector<void*> allocs;
+  size_t bytes_allocated = 0;
+  // a cache pass (refresh, or the block-diffusion prompt pass) has run since
+  // dllm_begin_decode over a canvas of this geometry
+  bool cache_ready = false;
+  int ready_batch = 0, ready_prompt = 0, ready_gen = 0;
   void* emb = nullptr;
   std::vector<float*> g_attn, g_ffn;
   float* g_final = nullptr;
@@ -164,11 +172,16 @@ struct dllm_ctx {
   dllm_status alloc(P** out, size_t bytes) {
     void* p = nullptr;
     bytes = bytes ? bytes : 16;
+    const uint64_t cap = g_device_limit.load();
+    if (cap && bytes_allocated + bytes > cap)
+      return fail(DLLM_ERR_OOM, "device allocation of " + std::to_string(bytes) + " bytes would exceed the limit of " +
+                                    std::to_string(cap) + " bytes set by dllm_set_device_limit");
     if (hipMalloc(&p, bytes) != hipSuccess) {
       (void)hipGetLastError();
       return fail(DLLM_ERR_OOM, "hipMalloc of " + std::to_string(bytes) + " bytes failed");
     }
     allocs.push_back(p);
+    bytes_allocated += bytes;
     if (hipMemsetAsync(p, 0, bytes, stream) != hipSuccess) return fail(DLLM_ERR_DEVICE, "hipMemsetAsync failed");
     *out = static_cast<P*>(p);
     return DLLM_OK;
@@ -249,6 +262,19 @@ dllm_status validate_decode(const dllm_ctx* ctx, const dllm_decode_cfg* d) {
   if ((d->rule == DLLM_RULE_TOPK || d->rule == DLLM_RULE_STEPS) && d->k < 1) return fail(DLLM_ERR_ARG, "k must be >= 1");
   if (d->refresh_every < 0) return fail(DLLM_ERR_ARG, "refresh_every must be >= 0");
   return DLLM_OK;
+}
+
+// A step that reads cached K/V (every mode but NONE) needs a cache pass over
+// a canvas of the same geometry since dllm_begin_decode.
+dllm_status check_cache_ready(const dllm_ctx* ctx, const dllm_decode_cfg* d, const char* what) {
+  if (d->cache == DLLM_CACHE_NONE) return DLLM_OK;
+  if (ctx->cache_ready && ctx->ready_batch == d->batch && ctx->ready_prompt == d->prompt_len &&
+      ctx->ready_gen == d->gen_len)
+    return DLLM_OK;
+  return fail(DLLM_ERR_STATE, std::string(what) +
+                                  ": the cache holds no K/V of this canvas (no dllm_refresh_cache since "
+                                  "dllm_begin_decode for this batch / prompt_len / gen_len; block diffusion "
+                                  "needs its prompt pass first)");
 }
 
 // ---------------------------------------------------------------------------
@@ -597,7 +623,7 @@ dllm_status refresh_impl(dllm_ctx* c, const dllm_canvas* cv, const dllm_decode_c
 // the LM-head reduction of block j's rows into c->conf / c->tok (no commit).
 template <typename T>
 dllm_status eval_block(dllm_ctx* c, const dllm_canvas* cv, const dllm_decode_cfg* d, int j, int cache,
-                       float* dbg_logits) {
+                       float* dbg_logits, hipEvent_t after_head = nullptr) {
   const dllm_model_cfg& m = c->cfg;
   Fwd f = make_fwd(c, cv, d);
   const int s = d->prompt_len + j * d->block_len;
@@ -630,22 +656,26 @@ dllm_status eval_block(dllm_ctx* c, const dllm_canvas* cv, const dllm_decode_cfg
                c->n_vtiles, c->pmax, c->psum, c->parg, dbg_logits, rowmap, count};
   TRY(launch_gemm<T>(c, DLLM_K_LMHEAD, compact ? c->xc : c->xh, c->wlm, HR, m.vocab, m.d_model, eh,
                      compact ? c->ssq_c : c->ssq_head, HR, count));
+  if (after_head) HIPCHK(hipEventRecord(after_head, c->stream));
   Timed tm(c, DLLM_K_MERGE, 12.0 * c->n_vtiles * HR + 8.0 * HR, 3.0 * c->n_vtiles * HR);
   hipLaunchKernelGGL(lm_merge_kernel, dim3(HR), dim3(kMergeThreads), 0, c->stream, c->pmax, c->psum, c->parg, c->n_vtiles,
                      HR, c->conf, c->tok, c->d_err, rowmap, count);
   return tm.done();
 }
 
+// ev (optional): three events recorded before the forward, after the LM-head
+// projection and after select/commit (the forward / selection split of a step).
 template <typename T>
 dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, int j, int* n_committed,
-                      int* block_done, float* dbg_logits, float* dbg_conf, int* dbg_tok) {
+                      int* block_done, float* dbg_logits, float* dbg_conf, int* dbg_tok, hipEvent_t* ev = nullptr) {
   const dllm_model_cfg& m = c->cfg;
   if (j < 0 || j >= d->gen_len / d->block_len) return fail(DLLM_ERR_ARG, "block_idx out of range");
   if ((cv->bias_target == nullptr) != (cv->bias_alpha == nullptr))
     return fail(DLLM_ERR_ARG, "bias_target and bias_alpha must both be set or both NULL");
   const int s = d->prompt_len + j * d->block_len;
   const int B = d->block_len, HR = d->batch * B;
-  TRY(eval_block<T>(c, cv, d, j, d->cache, dbg_logits));
+  if (ev) HIPCHK(hipEventRecord(ev[0], c->stream));
+  TRY(eval_block<T>(c, cv, d, j, d->cache, dbg_logits, ev ? ev[1] : nullptr));
   Fwd f = make_fwd(c, cv, d);
   SelectArgs sa{};
   sa.tokens = cv->tokens;
@@ -676,6 +706,7 @@ dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, in
     hipLaunchKernelGGL(select_commit_kernel, dim3(d->batch), dim3(256), 0, c->stream, sa);
     TRY(tm.done());
   }
+  if (ev) HIPCHK(hipEventRecord(ev[2], c->stream));
   const int mb = c->cfg.max_batch;
   HIPCHK(hipMemcpyAsync(c->h_pin, c->d_stat, (2 * (size_t)mb + 1) * sizeof(int), hipMemcpyDeviceToHost, c->stream));
   HIPCHK(hipStreamSynchronize(c->stream));
@@ -703,6 +734,9 @@ dllm_status staleness_impl(dllm_ctx* c, const dllm_canvas* cv, const dllm_decode
   const size_t slice = (size_t)d->batch * m.n_heads * c->seq_pad * m.head_dim;  // elements per layer
   const size_t es = sizeof(T);
   T* saved = nullptr;
+  const uint64_t cap = g_device_limit.load();
+  if (cap && c->bytes_allocated + 2 * slice * L * es > cap)
+    return fail(DLLM_ERR_OOM, "the K/V snapshot would exceed the limit set by dllm_set_device_limit");
   if (hipMalloc(&saved, 2 * slice * L * es) != hipSuccess) {
     (void)hipGetLastError();
     return fail(DLLM_ERR_OOM, "hipMalloc of the K/V snapshot failed");
@@ -761,7 +795,7 @@ dllm_status pack(dllm_ctx* c, const void* src, const void* src2, int rows, int K
   const size_t n = (size_t)rows * K;
   hipLaunchKernelGGL((pack_kernel<Tin, T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, c->stream,
                      static_cast<const Tin*>(src), static_cast<const Tin*>(src2), rows, K, mode, c->cfg.head_dim,
-                     static_cast<T*>(dst), row0);
+                     static_cast<T*>(dst), row0, c->d_err + 2);
   return check_launch();
 }
 
@@ -773,6 +807,11 @@ dllm_status init_impl(dllm_ctx* c, const void* const* t) {
   const size_t es = sizeof(T);
   for (int i = 0; i < 2 + 9 * L; ++i)
     if (!t[i]) return fail(DLLM_ERR_ARG, "tensor pointer " + std::to_string(i) + " is NULL");
+  // status block first: d_err[2] collects the packing range check
+  TRY(c->alloc(&c->d_stat, (2 * (size_t)m.max_batch + 4) * sizeof(int)));
+  c->d_ncommit = c->d_stat;
+  c->d_done = c->d_stat + m.max_batch;
+  c->d_err = c->d_stat + 2 * m.max_batch;
   auto gain = [&](const void* src, float** out) -> dllm_status {
     TRY(c->alloc(out, (size_t)d * sizeof(float)));
     hipLaunchKernelGGL((to_f32_kernel<Tin>), dim3(cdiv(d, 256)), dim3(256), 0, c->stream, static_cast<const Tin*>(src), *out, d);
@@ -850,17 +889,18 @@ dllm_status init_impl(dllm_ctx* c, const void* const* t) {
   TRY(c->alloc(&c->attn_ws, c->attn_ws_floats * sizeof(float)));
   c->gemm_part_floats = (size_t)16 << 20;
   TRY(c->alloc(&c->gemm_part, c->gemm_part_floats * sizeof(float)));
-  TRY(c->alloc(&c->d_stat, (2 * (size_t)m.max_batch + 4) * sizeof(int)));
-  c->d_ncommit = c->d_stat;
-  c->d_done = c->d_stat + m.max_batch;
-  c->d_err = c->d_stat + 2 * m.max_batch;
   TRY(c->alloc(&c->d_step, (size_t)m.max_batch * sizeof(int)));
   TRY(c->alloc(&c->d_blk_id, (size_t)m.max_batch * sizeof(int)));
   TRY(c->alloc(&c->d_blk_steps, (size_t)m.max_batch * sizeof(int)));
   hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, c->stream, c->d_blk_id, m.max_batch, -1);
   TRY(check_launch());
   HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&c->h_pin), (2 * m.max_batch + 4) * sizeof(int), hipHostMallocDefault));
+  HIPCHK(hipMemcpyAsync(c->h_pin, c->d_err + 2, sizeof(int), hipMemcpyDeviceToHost, c->stream));
   HIPCHK(hipStreamSynchronize(c->stream));
+  if (c->h_pin[0])
+    return fail(DLLM_ERR_ARG, c->bf16 ? "a weight is not finite or lies outside the fp16 range (|w| > 65504) the bf16 "
+                                        "model is computed in"
+                                      : "a weight is not finite");
   return DLLM_OK;
 }
 
@@ -994,22 +1034,63 @@ dllm_status dllm_refresh_cache(dllm_ctx* ctx, const dllm_canvas* canvas, const d
   g_err.clear();
   if (!ctx || !canvas || !canvas->tokens) return fail(DLLM_ERR_ARG, "ctx, canvas and canvas->tokens must be non-NULL");
   TRY(validate_decode(ctx, cfg));
+  const bool commit_pass = cfg->cache == DLLM_CACHE_BLOCK_CAUSAL && block_idx >= 0;
+  if (commit_pass) TRY(check_cache_ready(ctx, cfg, "commit pass"));
   ctx->timing_slot = DLLM_K_COUNT;
   const dllm_status s = ctx->bf16 ? refresh_impl<f16_t>(ctx, canvas, cfg, block_idx)
                                   : refresh_impl<float>(ctx, canvas, cfg, block_idx);
   ctx->timing_slot = 0;
+  if (s == DLLM_OK && !commit_pass) {
+    ctx->cache_ready = true;
+    ctx->ready_batch = cfg->batch;
+    ctx->ready_prompt = cfg->prompt_len;
+    ctx->ready_gen = cfg->gen_len;
+  }
   return s;
 }
 
-dllm_status dllm_block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg* cfg, int32_t block_idx,
-                            int32_t* n_committed, int32_t* block_done, float* dbg_logits, float* dbg_conf,
-                            int32_t* dbg_tok) {
+void dllm_set_device_limit(uint64_t bytes) { g_device_limit.store(bytes); }
+
+}  // extern "C"
+
+namespace {
+dllm_status block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg* cfg, int32_t block_idx,
+                       int32_t* n_committed, int32_t* block_done, float* dbg_logits, float* dbg_conf, int32_t* dbg_tok,
+                       hipEvent_t* ev) {
   g_err.clear();
   if (!ctx || !canvas || !canvas->tokens) return fail(DLLM_ERR_ARG, "ctx, canvas and canvas->tokens must be non-NULL");
   TRY(validate_decode(ctx, cfg));
   if ((dbg_conf == nullptr) != (dbg_tok == nullptr)) return fail(DLLM_ERR_ARG, "dbg_conf and dbg_tok must both be set or both NULL");
-  return ctx->bf16 ? step_impl<f16_t>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok)
-                   : step_impl<float>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok);
+  TRY(check_cache_ready(ctx, cfg, "dllm_block_step"));
+  return ctx->bf16 ? step_impl<f16_t>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok, ev)
+                   : step_impl<float>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok, ev);
+}
+
+// HIP events owned for the duration of one call
+struct Events {
+  hipEvent_t e[5] = {};
+  dllm_status create() {
+    for (auto& x : e) HIPCHK(hipEventCreate(&x));
+    return DLLM_OK;
+  }
+  ~Events() {
+    for (auto x : e)
+      if (x) (void)hipEventDestroy(x);
+  }
+  double ms(int a, int b, dllm_status* st) const {
+    float v = 0.f;
+    if (hipEventElapsedTime(&v, e[a], e[b]) != hipSuccess) *st = fail(DLLM_ERR_DEVICE, "hipEventElapsedTime failed");
+    return v;
+  }
+};
+}  // namespace
+
+extern "C" {
+
+dllm_status dllm_block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg* cfg, int32_t block_idx,
+                            int32_t* n_committed, int32_t* block_done, float* dbg_logits, float* dbg_conf,
+                            int32_t* dbg_tok) {
+  return block_step(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok, nullptr);
 }
 
 dllm_status dllm_staleness(dllm_ctx* ctx, const dllm_canvas* canvas, const dllm_decode_cfg* cfg, int32_t block_idx,
@@ -1018,6 +1099,7 @@ dllm_status dllm_staleness(dllm_ctx* ctx, const dllm_canvas* canvas, const dllm_
   g_err.clear();
   if (!ctx || !canvas || !canvas->tokens) return fail(DLLM_ERR_ARG, "ctx, canvas and canvas->tokens must be non-NULL");
   TRY(validate_decode(ctx, cfg));
+  TRY(check_cache_ready(ctx, cfg, "dllm_staleness"));
   return ctx->bf16 ? staleness_impl<f16_t>(ctx, canvas, cfg, block_idx, conf_cached, tok_cached, conf_fresh, tok_fresh,
                                            k_cos, v_cos)
                    : staleness_impl<float>(ctx, canvas, cfg, block_idx, conf_cached, tok_cached, conf_fresh, tok_fresh,
@@ -1042,6 +1124,7 @@ dllm_status dllm_begin_decode(dllm_ctx* ctx, const dllm_canvas* canvas, const dl
   TRY(check_launch());
   HIPCHK(hipMemcpyAsync(ctx->h_pin + 2 * m.max_batch + 1, ctx->d_err + 1, sizeof(int), hipMemcpyDeviceToHost, ctx->stream));
   HIPCHK(hipStreamSynchronize(ctx->stream));
+  ctx->cache_ready = false;
   if (ctx->h_pin[2 * m.max_batch + 1])
     return fail(DLLM_ERR_ARG, "canvas must hold prompt tokens (no mask_id, in vocab) followed by gen_len mask_id");
   return DLLM_OK;
@@ -1051,25 +1134,25 @@ dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cf
   const auto t_start = std::chrono::steady_clock::now();
   TRY(dllm_begin_decode(ctx, canvas, cfg));
 
-  hipEvent_t e0, e1;
-  HIPCHK(hipEventCreate(&e0));
-  HIPCHK(hipEventCreate(&e1));
-  double ms_refresh = 0.0;
+  // e[0], e[1]: around a cache pass; e[2..4]: a step's forward / selection split
+  Events ev;
+  TRY(ev.create());
+  hipEvent_t* step_ev = stats ? ev.e + 2 : nullptr;
+  double ms_refresh = 0.0, ms_step = 0.0, ms_select = 0.0;
   int64_t steps = 0, refreshes = 0, committed = 0;
   std::vector<int> nc(cfg->batch), done(cfg->batch), was_done(cfg->batch);
   std::vector<int64_t> seq_steps(cfg->batch, 0);
   const bool steps_rule = cfg->rule == DLLM_RULE_STEPS;
   const int max_in_block = steps_rule ? cfg->k : cfg->block_len;
   auto timed_refresh = [&](int blk) -> dllm_status {
-    HIPCHK(hipEventRecord(e0, ctx->stream));
+    HIPCHK(hipEventRecord(ev.e[0], ctx->stream));
     TRY(dllm_refresh_cache(ctx, canvas, cfg, blk));
-    HIPCHK(hipEventRecord(e1, ctx->stream));
-    HIPCHK(hipEventSynchronize(e1));
-    float ms = 0.f;
-    HIPCHK(hipEventElapsedTime(&ms, e0, e1));
-    ms_refresh += ms;
+    HIPCHK(hipEventRecord(ev.e[1], ctx->stream));
+    HIPCHK(hipEventSynchronize(ev.e[1]));
+    dllm_status es = DLLM_OK;
+    ms_refresh += ev.ms(0, 1, &es);
     ++refreshes;
-    return DLLM_OK;
+    return es;
   };
   dllm_status st = DLLM_OK;
   const int nb = cfg->gen_len / cfg->block_len;
@@ -1085,8 +1168,13 @@ dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cf
         st = timed_refresh(0);
         if (st != DLLM_OK) break;
       }
-      st = dllm_block_step(ctx, canvas, cfg, j, nc.data(), done.data(), nullptr, nullptr, nullptr);
+      st = block_step(ctx, canvas, cfg, j, nc.data(), done.data(), nullptr, nullptr, nullptr, step_ev);
       if (st != DLLM_OK) break;
+      if (step_ev) {   // the step returned after its status readback: the events are complete
+        ms_step += ev.ms(2, 3, &st);
+        ms_select += ev.ms(3, 4, &st);
+        if (st != DLLM_OK) break;
+      }
       ++steps;
       ++in_block;
       bool all_done = true, stalled = false;
@@ -1108,8 +1196,6 @@ dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cf
     }
     if (st == DLLM_OK && bc) st = timed_refresh(j);
   }
-  (void)hipEventDestroy(e0);
-  (void)hipEventDestroy(e1);
   if (st != DLLM_OK) return st;
   if (stats) {
     stats->steps = steps;
@@ -1119,6 +1205,8 @@ dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cf
     for (int64_t v : seq_steps) mx = v > mx ? v : mx;
     stats->max_seq_steps = mx;
     stats->ms_refresh = ms_refresh;
+    stats->ms_step = ms_step;
+    stats->ms_select = ms_select;
     stats->ms_total = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();
   }
   return DLLM_OK;

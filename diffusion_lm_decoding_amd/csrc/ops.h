@@ -369,10 +369,12 @@ __global__ __launch_bounds__(256) void canvas_check_kernel(const int* tokens, in
 //           dst row h*dh + p <- src row h*dh + p/2 + (p%2)*(dh/2)
 //   mode 2: interleave: dst row 2i <- src row i, dst row 2i+1 <- src2 row i
 // Elements are converted from the input type Tin to the compute type T
-// (bf16 -> fp16 is exact except for |w| < 2^-17, which rounds to 2^-24 steps).
+// (bf16 -> fp16 is exact except for |w| < 2^-17, which rounds to 2^-24 steps);
+// a value that is not finite after the conversion (|w| > 65504 in fp16, or a
+// non-finite input) sets *range_err.
 template <typename Tin, typename T>
 __global__ __launch_bounds__(256) void pack_kernel(const Tin* src, const Tin* src2, int rows, int K,
-                                                   int mode, int dh, T* dst, int row0) {
+                                                   int mode, int dh, T* dst, int row0, int* range_err) {
   const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= (size_t)rows * K) return;
   const int r = (int)(t / K), k = (int)(t % K);
@@ -385,7 +387,9 @@ __global__ __launch_bounds__(256) void pack_kernel(const Tin* src, const Tin* sr
     s = (r & 1) ? src2 : src;
     sr = r >> 1;
   }
-  dst[packed_off<T>(row0 + r, k, K)] = Elem<T>::cvt(Elem<Tin>::load(s + (size_t)sr * K + k));
+  const T v = Elem<T>::cvt(Elem<Tin>::load(s + (size_t)sr * K + k));
+  if (!(fabsf(Elem<T>::load(&v)) <= 3.0e38f)) atomicOr(range_err, 1);
+  dst[packed_off<T>(row0 + r, k, K)] = v;
 }
 
 __global__ __launch_bounds__(64) void fill_i32_kernel(int* p, int n, int v) {

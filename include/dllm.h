@@ -47,9 +47,12 @@ extern "C" {
 typedef enum {
   DLLM_OK = 0,
   DLLM_ERR_ARG = 1,      /* invalid argument or configuration                 */
-  DLLM_ERR_OOM = 2,      /* device allocation failed                          */
+  DLLM_ERR_OOM = 2,      /* device allocation failed, or it would exceed the
+                            limit set by dllm_set_device_limit                */
   DLLM_ERR_DEVICE = 3,   /* a HIP call failed                                 */
-  DLLM_ERR_STATE = 4,    /* call out of order, or a step committed nothing    */
+  DLLM_ERR_STATE = 4,    /* call out of order (a step or commit pass with no
+                            cache pass over the canvas since
+                            dllm_begin_decode), or a step committed nothing   */
   DLLM_ERR_NUMERIC = 5   /* non-finite logits / confidences were produced     */
 } dllm_status;
 
@@ -156,13 +159,25 @@ typedef struct {
   int32_t* commit_step;
 } dllm_canvas;
 
+/* Decode statistics.  The three device-time fields follow the cost split of
+ * [RN] sec. 7, eq. (15): T = S C_active + R + T_selection.
+ *   ms_step    S C_active: the denoising steps' forward passes, from the
+ *              embedding through the LM-head projection of the masked rows;
+ *   ms_refresh R: refresh, prompt and commit passes;
+ *   ms_select  T_selection: turning the LM-head partials into (argmax,
+ *              confidence) and applying the rule (merge + select/commit);
+ * each the summed device time between HIP events on the context's stream.
+ * ms_total - (ms_step + ms_refresh + ms_select) is host time: launches and
+ * the per-step status readback. */
 typedef struct {
   int64_t steps;          /* denoising steps (forward passes with a commit)   */
   int64_t refreshes;      /* full-canvas K/V refresh passes                   */
   int64_t committed;      /* tokens committed over all sequences              */
   int64_t max_seq_steps;  /* largest per-sequence step count                  */
   double ms_total;        /* wall time of the call                            */
-  double ms_refresh;      /* time in refresh / prefill / commit passes        */
+  double ms_refresh;      /* device time in refresh / prefill / commit passes */
+  double ms_step;         /* device time in the steps' forward passes         */
+  double ms_select;       /* device time in LM-head merge + select/commit     */
 } dllm_stats;
 
 typedef struct dllm_ctx dllm_ctx;
@@ -179,7 +194,9 @@ typedef struct dllm_ctx dllm_ctx;
  *   gains included.  The weights are copied into the context's packed layout;
  *   the caller may free its tensors when the call returns.
  *   hip_stream: hipStream_t on which all later work runs (NULL = default).
- * Errors: DLLM_ERR_ARG (unsupported shape, NULL pointer), DLLM_ERR_OOM,
+ * Errors: DLLM_ERR_ARG (unsupported shape, NULL pointer, a weight that is not
+ *   finite or - for DLLM_BF16, computed in fp16 - has |w| > 65504),
+ *   DLLM_ERR_OOM (also when the context would exceed dllm_set_device_limit),
  *   DLLM_ERR_DEVICE.  *out is NULL on failure. */
 dllm_status dllm_init_weights(dllm_ctx** out, const dllm_model_cfg* cfg,
                               const void* const* tensors, void* hip_stream);
@@ -193,8 +210,12 @@ dllm_status dllm_init_weights(dllm_ctx** out, const dllm_model_cfg* cfg,
  *     only, bidirectional among themselves); block_idx = j >= 0 runs the
  *     commit pass of answer block j: its final tokens attend to [0, end of
  *     block j) and their exact K/V are stored ([DS] KV-cache section).
+ * A pass over the whole canvas, or the prompt pass, marks the cache as holding
+ * K/V of a canvas of this batch / prompt_len / gen_len (what dllm_block_step
+ * and the commit pass require).
  * Errors: DLLM_ERR_ARG (bad cfg, batch > max_batch, seq > max_seq),
- *   DLLM_ERR_DEVICE. */
+ *   DLLM_ERR_STATE (a commit pass with no prompt pass since
+ *   dllm_begin_decode), DLLM_ERR_DEVICE. */
 dllm_status dllm_refresh_cache(dllm_ctx* ctx, const dllm_canvas* canvas,
                                const dllm_decode_cfg* cfg, int32_t block_idx);
 
@@ -213,8 +234,10 @@ dllm_status dllm_refresh_cache(dllm_ctx* ctx, const dllm_canvas* canvas,
  *   dbg_conf, dbg_tok: device float / int32 [batch * block_len] or NULL:
  *     c_i and y_i of the block's masked rows (-1 for rows already committed).
  * Blocks the host until the 8-byte-per-sequence result is read back.
- * Errors: DLLM_ERR_ARG, DLLM_ERR_NUMERIC (non-finite confidence; the canvas is
- *   left unchanged), DLLM_ERR_DEVICE. */
+ * Errors: DLLM_ERR_ARG, DLLM_ERR_STATE (cache modes other than NONE: no
+ *   dllm_refresh_cache over a canvas of this batch / prompt_len / gen_len
+ *   since dllm_begin_decode - block diffusion: no prompt pass), DLLM_ERR_NUMERIC
+ *   (non-finite confidence; the canvas is left unchanged), DLLM_ERR_DEVICE. */
 dllm_status dllm_block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg* cfg,
                             int32_t block_idx, int32_t* n_committed, int32_t* block_done,
                             float* dbg_logits, float* dbg_conf, int32_t* dbg_tok);
@@ -237,8 +260,8 @@ dllm_status dllm_block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decod
  *   k_cos, v_cos: device float [n_layers, batch, prompt_len + gen_len] or NULL:
  *     <cached, fresh> / (|cached| |fresh|) over all heads of the position
  *     (1 if both are zero, 0 if one is).
- * Blocks until done.  Errors: DLLM_ERR_ARG, DLLM_ERR_OOM, DLLM_ERR_NUMERIC,
- *   DLLM_ERR_DEVICE. */
+ * Blocks until done.  Errors: DLLM_ERR_ARG, DLLM_ERR_STATE (as
+ *   dllm_block_step), DLLM_ERR_OOM, DLLM_ERR_NUMERIC, DLLM_ERR_DEVICE. */
 dllm_status dllm_staleness(dllm_ctx* ctx, const dllm_canvas* canvas, const dllm_decode_cfg* cfg, int32_t block_idx,
                            float* conf_cached, int32_t* tok_cached, float* conf_fresh, int32_t* tok_fresh,
                            float* k_cos, float* v_cos);
@@ -247,6 +270,7 @@ dllm_status dllm_staleness(dllm_ctx* ctx, const dllm_canvas* canvas, const dllm_
  * dllm_block_step: checks that the prompt holds no mask_id (and lies in
  * [0, vocab)) and the answer region is all mask_id, and resets the
  * per-sequence step counters (commit_step numbering, the STEPS schedule).
+ * The cache counts as empty afterwards (the next step needs a cache pass).
  * dllm_decode does this itself.  Errors: DLLM_ERR_ARG, DLLM_ERR_DEVICE. */
 dllm_status dllm_begin_decode(dllm_ctx* ctx, const dllm_canvas* canvas, const dllm_decode_cfg* cfg);
 
@@ -309,6 +333,14 @@ dllm_status dllm_get_timing(dllm_ctx* ctx, dllm_kernel_time* out, int32_t reset)
  * of register-resident 32x32x16 fp16 MFMA chains on every CU.  Either output may be NULL.
  * Errors: DLLM_ERR_ARG (bytes < 1 MiB), DLLM_ERR_OOM, DLLM_ERR_DEVICE. */
 dllm_status dllm_probe_peaks(uint64_t bytes, double* hbm_gbs, double* mfma_f16_tflops);
+
+/* Process-wide cap on the device memory a context may hold: dllm_init_weights
+ * fails with DLLM_ERR_OOM, before allocating past it, when the packed weights,
+ * KV cache and workspaces of the requested shape exceed `bytes`, and
+ * dllm_staleness does the same for its snapshot; contexts created earlier are
+ * not affected.  0 (the default) removes the cap.  For callers that budget
+ * device memory, and to exercise the out-of-memory path. */
+void dllm_set_device_limit(uint64_t bytes);
 
 /* Release every device allocation of the context.  NULL is ignored. */
 void dllm_destroy(dllm_ctx* ctx);

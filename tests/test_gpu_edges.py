@@ -47,7 +47,7 @@ def test_ragged_sizes_lockstep(engines, dtype, cache):
     cv = eng.canvas(pr, t, a, 21)
     fp32 = dtype == "f32"
     rep = replay(eng, cv, cfg, om, pr, t, a, cache, "threshold", tol=Tol(fp32=fp32), seq=2)
-    print(f"{dtype}/{cache}: steps={rep.steps} max|dlogit|={rep.max_logit_err:.3g} exempt={rep.exempt}", flush=True)
+    print(f"{dtype}/{cache}: {rep.summary()}", flush=True)
     assert not rep.bad, rep.bad[:5]
     assert rep.steps >= 3
     if fp32:
@@ -161,6 +161,6 @@ def test_masked_row_lm_head_lockstep_bf16(engines, cache):
     cfg = Engine.decode_cfg(4, 16, 64, 32, cache=cache)
     cv = eng.canvas(pr, t, a, 64)
     rep = replay(eng, cv, cfg, om, pr, t, a, cache, "threshold", tol=Tol(fp32=False), seq=3, max_steps=12)
-    print(f"bf16/{cache}: steps={rep.steps} max|dlogit|={rep.max_logit_err:.3g} exempt={rep.exempt}", flush=True)
+    print(f"bf16/{cache}: {rep.summary()}", flush=True)
     assert not rep.bad, rep.bad[:5]
     assert rep.steps >= 3 and rep.max_logit_err < 5e-2

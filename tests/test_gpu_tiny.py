@@ -78,6 +78,7 @@ def test_bf16_lockstep(engines, cache, rule, kw):
     cfg = Engine.decode_cfg(3, 40, 48, 16, cache=cache, rule=rule, **kw)
     cv = eng.canvas(pr, t, a, 48)
     rep = replay(eng, cv, cfg, om, pr, t, a, cache, rule, tol=Tol(fp32=False), seq=2, **kw)
+    print(f"bf16 {cache}/{rule}: {rep.summary()}", flush=True)
     assert not rep.bad, rep.bad[:5]
     assert rep.max_logit_err < 5e-2 and rep.max_conf_err < 1e-2
 
@@ -133,6 +134,50 @@ def test_refresh_every_step_equals_uncached_on_gpu(engines):
     eng.decode(c2, Engine.decode_cfg(1, 32, 64, 16, cache="dual", refresh_every=1))
     assert np.array_equal(c1.tokens.cpu().numpy(), c2.tokens.cpu().numpy())
     assert np.array_equal(c1.commit_step.cpu().numpy(), c2.commit_step.cpu().numpy())
+
+
+@pytest.mark.parametrize("cache", ["dual", "prefix"])
+@pytest.mark.parametrize("r", [2, 4])
+def test_refresh_every_full_decode_matches_oracle(engines, cache, r):
+    """Refresh interval r inside a block (reading notes sec. 11): whole
+    dllm_decode runs (batch 2) give the oracle's tokens, per-position commit
+    steps and, per sequence, step counts; the batch-1 refresh count is the
+    oracle's."""
+    from diffusion_lm_decoding_amd.engine import Engine
+    eng, om = engines["f32"]
+    pr, t, a = _inputs(2, 32, 64, seed=63 + r, alpha_max=16.0)
+    cv = eng.canvas(pr, t, a, 64)
+    stats = eng.decode(cv, Engine.decode_cfg(2, 32, 64, 16, cache=cache, refresh_every=r))
+    toks, cs = cv.tokens.cpu().numpy(), cv.commit_step.cpu().numpy()
+    dec = OracleDecoder(om, 32, 64, 16, cache=cache, refresh_every=r)
+    steps = []
+    for b in range(2):
+        st = dec.decode(pr[b], t[b], a[b])
+        assert np.array_equal(toks[b], st.canvas), f"sequence {b}"
+        for k, rec in enumerate(st.records):
+            assert (cs[b, rec.selected - 32] == k).all()
+        steps.append(st.steps)
+    assert stats.max_seq_steps == max(steps)
+    c1 = eng.canvas(pr[:1], t[:1], a[:1], 64)
+    s1 = eng.decode(c1, Engine.decode_cfg(1, 32, 64, 16, cache=cache, refresh_every=r))
+    o1 = dec.decode(pr[0], t[0], a[0])
+    assert s1.refreshes == o1.refreshes and s1.steps == o1.steps
+    assert o1.refreshes > 4             # the interval fired inside blocks
+
+
+@pytest.mark.parametrize("cache", ["dual", "prefix"])
+@pytest.mark.parametrize("r", [2, 4])
+def test_refresh_every_lockstep_f32(engines, cache, r):
+    """The same interval in lock-step: every step's logits within 1e-4 of the
+    row scale and every decision identical (fp32: no exemption)."""
+    from diffusion_lm_decoding_amd.engine import Engine
+    eng, om = engines["f32"]
+    pr, t, a = _inputs(2, 32, 64, seed=73 + r, alpha_max=16.0)
+    cfg = Engine.decode_cfg(2, 32, 64, 16, cache=cache, refresh_every=r)
+    cv = eng.canvas(pr, t, a, 64)
+    rep = replay(eng, cv, cfg, om, pr, t, a, cache, "threshold", tol=Tol(fp32=True), seq=1, refresh_every=r)
+    assert not rep.bad, rep.bad[:5]
+    assert rep.steps >= 8 and rep.max_logit_err < 1e-4 and rep.exempt == 0
 
 
 def test_schedules_on_gpu(engines):
