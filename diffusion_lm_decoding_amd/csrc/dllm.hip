@@ -1061,6 +1061,7 @@ dllm_status block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg
   if (!ctx || !canvas || !canvas->tokens) return fail(DLLM_ERR_ARG, "ctx, canvas and canvas->tokens must be non-NULL");
   TRY(validate_decode(ctx, cfg));
   if ((dbg_conf == nullptr) != (dbg_tok == nullptr)) return fail(DLLM_ERR_ARG, "dbg_conf and dbg_tok must both be set or both NULL");
+  if (block_idx < 0 || block_idx >= cfg->gen_len / cfg->block_len) return fail(DLLM_ERR_ARG, "block_idx out of range");
   TRY(check_cache_ready(ctx, cfg, "dllm_block_step"));
   return ctx->bf16 ? step_impl<f16_t>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok, ev)
                    : step_impl<float>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok, ev);
@@ -1099,6 +1100,9 @@ dllm_status dllm_staleness(dllm_ctx* ctx, const dllm_canvas* canvas, const dllm_
   g_err.clear();
   if (!ctx || !canvas || !canvas->tokens) return fail(DLLM_ERR_ARG, "ctx, canvas and canvas->tokens must be non-NULL");
   TRY(validate_decode(ctx, cfg));
+  if (block_idx < 0 || block_idx >= cfg->gen_len / cfg->block_len) return fail(DLLM_ERR_ARG, "block_idx out of range");
+  if (cfg->cache == DLLM_CACHE_BLOCK_CAUSAL)
+    return fail(DLLM_ERR_ARG, "the block-causal cache is exact; staleness is defined for NONE, PREFIX and DUAL");
   TRY(check_cache_ready(ctx, cfg, "dllm_staleness"));
   return ctx->bf16 ? staleness_impl<f16_t>(ctx, canvas, cfg, block_idx, conf_cached, tok_cached, conf_fresh, tok_fresh,
                                            k_cos, v_cos)
@@ -1134,11 +1138,14 @@ dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cf
   const auto t_start = std::chrono::steady_clock::now();
   TRY(dllm_begin_decode(ctx, canvas, cfg));
 
-  // e[0], e[1]: around a cache pass; e[2..4]: a step's forward / selection split
+  // e[0], e[1]: around a cache pass; e[2..4]: a step's forward / selection
+  // split, taken on every kSplitEvery-th step only (each event pair lengthens
+  // the launch gaps around it by microseconds) and scaled to all steps
+  constexpr int64_t kSplitEvery = 8;
   Events ev;
   TRY(ev.create());
-  hipEvent_t* step_ev = stats ? ev.e + 2 : nullptr;
   double ms_refresh = 0.0, ms_step = 0.0, ms_select = 0.0;
+  int64_t split_steps = 0;
   int64_t steps = 0, refreshes = 0, committed = 0;
   std::vector<int> nc(cfg->batch), done(cfg->batch), was_done(cfg->batch);
   std::vector<int64_t> seq_steps(cfg->batch, 0);
@@ -1168,11 +1175,13 @@ dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cf
         st = timed_refresh(0);
         if (st != DLLM_OK) break;
       }
+      hipEvent_t* step_ev = (stats && steps % kSplitEvery == 0) ? ev.e + 2 : nullptr;
       st = block_step(ctx, canvas, cfg, j, nc.data(), done.data(), nullptr, nullptr, nullptr, step_ev);
       if (st != DLLM_OK) break;
       if (step_ev) {   // the step returned after its status readback: the events are complete
         ms_step += ev.ms(2, 3, &st);
         ms_select += ev.ms(3, 4, &st);
+        ++split_steps;
         if (st != DLLM_OK) break;
       }
       ++steps;
@@ -1205,8 +1214,9 @@ dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cf
     for (int64_t v : seq_steps) mx = v > mx ? v : mx;
     stats->max_seq_steps = mx;
     stats->ms_refresh = ms_refresh;
-    stats->ms_step = ms_step;
-    stats->ms_select = ms_select;
+    const double scale = split_steps ? (double)steps / (double)split_steps : 0.0;
+    stats->ms_step = ms_step * scale;
+    stats->ms_select = ms_select * scale;
     stats->ms_total = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();
   }
   return DLLM_OK;

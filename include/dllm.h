@@ -166,9 +166,11 @@ typedef struct {
  *   ms_refresh R: refresh, prompt and commit passes;
  *   ms_select  T_selection: turning the LM-head partials into (argmax,
  *              confidence) and applying the rule (merge + select/commit);
- * each the summed device time between HIP events on the context's stream.
- * ms_total - (ms_step + ms_refresh + ms_select) is host time: launches and
- * the per-step status readback. */
+ * each the device time between HIP events on the context's stream: every
+ * cache pass is timed; the step split is timed on every 8th denoising step
+ * (the 1st, 9th, ...) and scaled to all steps, since each event lengthens the
+ * launch gaps around it by microseconds.  ms_total - (ms_step + ms_refresh +
+ * ms_select) is host time: launches and the per-step status readback. */
 typedef struct {
   int64_t steps;          /* denoising steps (forward passes with a commit)   */
   int64_t refreshes;      /* full-canvas K/V refresh passes                   */

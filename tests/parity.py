@@ -22,8 +22,13 @@ the error budget when it lies within 0.02 of the oracle's confidence at the
 cut (or the cut itself moved: the rule's criterion at the larger of the two
 counts lies within 0.02 (n+1) of its bound).  A token difference is exempt
 only when the oracle's top-2 probability gap is <= 0.05.  Exemptions are
-counted per kind; `Report.check_exemptions` bounds each at 1% of the
-decisions (at least one)."""
+counted per kind (selection; token of a committed position);
+`Report.check_exemptions` bounds each at 1% of the decisions (at least one).
+An argmax difference at a candidate that neither side commits this step
+decides nothing; it is still allowed only at a top-2 gap <= 0.05, and is
+counted apart (at random initialisation with a 126k vocabulary the top two
+logits of a low-confidence row lie within the fp16 rounding of each other
+for a few percent of rows)."""
 from __future__ import annotations
 
 import math
@@ -54,6 +59,7 @@ class Report:
     decisions: int = 0
     exempt_sel: int = 0
     exempt_tok: int = 0
+    argmax_flips: int = 0          # uncommitted candidates whose argmax differs (near-ties)
     bad: List[str] = field(default_factory=list)
 
     @property
@@ -62,7 +68,8 @@ class Report:
 
     def summary(self) -> str:
         return (f"steps={self.steps} max|dlogit|={self.max_logit_err:.3g} max|dconf|={self.max_conf_err:.3g} "
-                f"decisions={self.decisions} exempt_selection={self.exempt_sel} exempt_token={self.exempt_tok}")
+                f"decisions={self.decisions} exempt_selection={self.exempt_sel} exempt_token={self.exempt_tok} "
+                f"argmax_flips_uncommitted={self.argmax_flips}")
 
     def check_exemptions(self, frac: float = 0.01) -> None:
         cap = max(1, math.floor(frac * self.decisions))
@@ -202,11 +209,14 @@ def compare_step(rep: Report, tol: Tol, dec: OracleDecoder, cand, y, c, l, gc, g
             rep.exempt_sel += 1
         else:
             rep.bad.append(f"{tag}: selection differs at {pos} ({why})")
+    committed = set(g_sel.tolist()) | set(o_sel.tolist())
     for i in np.nonzero(gt != y)[0]:
         if tol.fp32 or gap[i] > tol.top2_gap:
             rep.bad.append(f"{tag}: argmax differs at {cand[i]}: gpu {gt[i]} oracle {y[i]} (top-2 gap {gap[i]:.3g})")
+        elif int(cand[i]) in committed:
+            rep.exempt_tok += 1        # a committed token differs at a near-tie
         else:
-            rep.exempt_tok += 1
+            rep.argmax_flips += 1      # not committed this step: no decision taken on it
 
 
 def replay(engine, cv, cfg, model: OracleModel, prompt, target, alpha, cache, rule, tau=0.9,
