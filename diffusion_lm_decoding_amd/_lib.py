@@ -18,7 +18,8 @@ F32, BF16 = 0, 1
 CACHE = {"none": 0, "prefix": 1, "dual": 2, "block_causal": 3}
 RULE = {"threshold": 0, "factor": 1, "topk": 2, "budget": 3, "steps": 4}
 
-SYMBOLS = ("dllm_init_weights", "dllm_refresh_cache", "dllm_block_step", "dllm_staleness", "dllm_begin_decode",
+SYMBOLS = ("dllm_init_weights", "dllm_refresh_cache", "dllm_block_step", "dllm_block_step_noalloc",
+           "dllm_staleness", "dllm_begin_decode",
            "dllm_decode", "dllm_set_timing", "dllm_get_timing", "dllm_probe_peaks", "dllm_set_device_limit",
            "dllm_destroy", "dllm_last_error")
 KERNEL_CLASSES = ("embed", "rmsnorm", "qkv", "attn", "oproj", "gateup", "down", "lmhead", "merge",
@@ -80,6 +81,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.dllm_block_step.argtypes = [P, C.POINTER(Canvas), C.POINTER(DecodeCfg), C.c_int32,
                                     C.POINTER(C.c_int32), C.POINTER(C.c_int32), P, P, P]
     lib.dllm_block_step.restype = C.c_int
+    lib.dllm_block_step_noalloc.argtypes = lib.dllm_block_step.argtypes
+    lib.dllm_block_step_noalloc.restype = C.c_int
     lib.dllm_staleness.argtypes = [P, C.POINTER(Canvas), C.POINTER(DecodeCfg), C.c_int32, P, P, P, P, P, P]
     lib.dllm_staleness.restype = C.c_int
     lib.dllm_begin_decode.argtypes = [P, C.POINTER(Canvas), C.POINTER(DecodeCfg)]
@@ -124,6 +127,13 @@ def dllm_block_step(ctx: int, canvas: Canvas, cfg: DecodeCfg, block_idx: int, n_
     check(load().dllm_block_step(C.c_void_p(ctx), C.byref(canvas), C.byref(cfg), block_idx,
                                  n_committed, block_done, C.c_void_p(dbg_logits),
                                  C.c_void_p(dbg_conf), C.c_void_p(dbg_tok)))
+
+
+def dllm_block_step_noalloc(ctx: int, canvas: Canvas, cfg: DecodeCfg, block_idx: int, n_committed=None,
+                            block_done=None, dbg_logits=0, dbg_conf=0, dbg_tok=0) -> None:
+    check(load().dllm_block_step_noalloc(C.c_void_p(ctx), C.byref(canvas), C.byref(cfg), block_idx,
+                                         n_committed, block_done, C.c_void_p(dbg_logits),
+                                         C.c_void_p(dbg_conf), C.c_void_p(dbg_tok)))
 
 
 def dllm_staleness(ctx: int, canvas: Canvas, cfg: DecodeCfg, block_idx: int, conf_cached=0, tok_cached=0,

@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <atomic>
 #include <chrono>
+#include <mutex>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -60,8 +61,38 @@ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 }  // namespace
 
+// Scratch of dllm_block_step_noalloc: one copy per GPU, alive until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device array: the device address comes from hipGetSymbolAddress, taken
+// once per device when a context is created on it (scratch_address below).
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on first use).
+dllm_status scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(DLLM_ERR_DEVICE, "device ordinal out of range");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DLLM_ERR_DEVICE, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DLLM_OK;
+}
+}  // namespace
+
 struct dllm_ctx {
   dllm_model_cfg cfg{};
+  int device = 0;
+  float* scratch_dev = nullptr;   // this device's `scratch` (dllm_block_step_noalloc)
   hipStream_t stream = nullptr;
   bool bf16 = true;
   int esz = 2;
@@ -457,7 +488,25 @@ struct Fwd {
   bool kv_only;         // last layer: K/V only (cache passes)
   int head_blk;         // > 0: rows [head_off, head_off + head_blk) of each
   int head_off;         //      sequence feed the LM head
+  float* attn_ws;       // attention key-share partials
+  size_t attn_ws_floats;
 };
+
+// Per-step workspaces: the context's own (dllm_block_step) or slices of the
+// static scratch (dllm_block_step_noalloc).
+struct StepWs {
+  float* attn_ws;
+  size_t attn_ws_floats;
+  float* pmax;
+  float* psum;
+  int* parg;
+  float* conf;
+  int* tok;
+};
+
+StepWs ctx_ws(const dllm_ctx* c) {
+  return StepWs{c->attn_ws, c->attn_ws_floats, c->pmax, c->psum, c->parg, c->conf, c->tok};
+}
 
 template <typename T, int DH>
 dllm_status launch_attn(dllm_ctx* c, int layer, const Fwd& f) {
@@ -482,10 +531,10 @@ dllm_status launch_attn(dllm_ctx* c, int layer, const Fwd& f) {
   int splits = 1;
   while (nwg * splits < 256 && ntile / (splits * 2) >= 3 && splits < kMaxAttnSplits) splits *= 2;
   const size_t rec = (size_t)(DH / 32 * 16 + 2) * 64;
-  while (splits > 1 && (size_t)splits * nwg * rec > c->attn_ws_floats) splits /= 2;
+  while (splits > 1 && (size_t)splits * nwg * rec > f.attn_ws_floats) splits /= 2;
   a.splits = splits;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)DH));
-  a.ws = c->attn_ws;
+  a.ws = f.attn_ws;
   // algorithmic: K and V of the keys each 32-query block attends read once, Q read, O written
   double kv = 0.0, fl = 0.0;
   for (int qb = 0; qb < a.qblocks; ++qb) {
@@ -584,8 +633,9 @@ dllm_status forward(dllm_ctx* c, const Fwd& f) {
 }
 
 Fwd make_fwd(const dllm_ctx* c, const dllm_canvas* cv, const dllm_decode_cfg* d) {
-  (void)c;
   Fwd f{};
+  f.attn_ws = c->attn_ws;
+  f.attn_ws_floats = c->attn_ws_floats;
   f.tokens = cv->tokens;
   f.seq_len = d->prompt_len + d->gen_len;
   f.batch = d->batch;
@@ -623,9 +673,11 @@ dllm_status refresh_impl(dllm_ctx* c, const dllm_canvas* cv, const dllm_decode_c
 // the LM-head reduction of block j's rows into c->conf / c->tok (no commit).
 template <typename T>
 dllm_status eval_block(dllm_ctx* c, const dllm_canvas* cv, const dllm_decode_cfg* d, int j, int cache,
-                       float* dbg_logits, hipEvent_t after_head = nullptr) {
+                       float* dbg_logits, const StepWs& ws, hipEvent_t after_head = nullptr) {
   const dllm_model_cfg& m = c->cfg;
   Fwd f = make_fwd(c, cv, d);
+  f.attn_ws = ws.attn_ws;
+  f.attn_ws_floats = ws.attn_ws_floats;
   const int s = d->prompt_len + j * d->block_len;
   switch (cache) {
     case DLLM_CACHE_NONE: f.row_start = 0; f.nr = f.seq_len; break;
@@ -653,13 +705,13 @@ dllm_status eval_block(dllm_ctx* c, const dllm_canvas* cv, const dllm_decode_cfg
   }
   TRY(check_launch());
   EpiLMHead eh{HR, B, d->gen_len, s - d->prompt_len, cv->bias_target, cv->bias_alpha, m.mask_id, m.vocab,
-               c->n_vtiles, c->pmax, c->psum, c->parg, dbg_logits, rowmap, count};
+               c->n_vtiles, ws.pmax, ws.psum, ws.parg, dbg_logits, rowmap, count};
   TRY(launch_gemm<T>(c, DLLM_K_LMHEAD, compact ? c->xc : c->xh, c->wlm, HR, m.vocab, m.d_model, eh,
                      compact ? c->ssq_c : c->ssq_head, HR, count));
   if (after_head) HIPCHK(hipEventRecord(after_head, c->stream));
   Timed tm(c, DLLM_K_MERGE, 12.0 * c->n_vtiles * HR + 8.0 * HR, 3.0 * c->n_vtiles * HR);
-  hipLaunchKernelGGL(lm_merge_kernel, dim3(HR), dim3(kMergeThreads), 0, c->stream, c->pmax, c->psum, c->parg, c->n_vtiles,
-                     HR, c->conf, c->tok, c->d_err, rowmap, count);
+  hipLaunchKernelGGL(lm_merge_kernel, dim3(HR), dim3(kMergeThreads), 0, c->stream, ws.pmax, ws.psum, ws.parg,
+                     c->n_vtiles, HR, ws.conf, ws.tok, c->d_err, rowmap, count);
   return tm.done();
 }
 
@@ -667,7 +719,8 @@ dllm_status eval_block(dllm_ctx* c, const dllm_canvas* cv, const dllm_decode_cfg
 // projection and after select/commit (the forward / selection split of a step).
 template <typename T>
 dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, int j, int* n_committed,
-                      int* block_done, float* dbg_logits, float* dbg_conf, int* dbg_tok, hipEvent_t* ev = nullptr) {
+                      int* block_done, float* dbg_logits, float* dbg_conf, int* dbg_tok, const StepWs& ws,
+                      hipEvent_t* ev = nullptr) {
   const dllm_model_cfg& m = c->cfg;
   if (j < 0 || j >= d->gen_len / d->block_len) return fail(DLLM_ERR_ARG, "block_idx out of range");
   if ((cv->bias_target == nullptr) != (cv->bias_alpha == nullptr))
@@ -675,7 +728,7 @@ dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, in
   const int s = d->prompt_len + j * d->block_len;
   const int B = d->block_len, HR = d->batch * B;
   if (ev) HIPCHK(hipEventRecord(ev[0], c->stream));
-  TRY(eval_block<T>(c, cv, d, j, d->cache, dbg_logits, ev ? ev[1] : nullptr));
+  TRY(eval_block<T>(c, cv, d, j, d->cache, dbg_logits, ws, ev ? ev[1] : nullptr));
   Fwd f = make_fwd(c, cv, d);
   SelectArgs sa{};
   sa.tokens = cv->tokens;
@@ -685,8 +738,8 @@ dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, in
   sa.blk = B;
   sa.start = s;
   sa.mask_id = m.mask_id;
-  sa.conf = c->conf;
-  sa.tok = c->tok;
+  sa.conf = ws.conf;
+  sa.tok = ws.tok;
   sa.rule = d->rule;
   sa.tau = d->tau;
   sa.factor = d->factor;
@@ -756,11 +809,11 @@ dllm_status staleness_impl(dllm_ctx* c, const dllm_canvas* cv, const dllm_decode
   auto body = [&]() -> dllm_status {
     TRY(copy_kv(true));
     const int B = d->block_len;
-    TRY(eval_block<T>(c, cv, d, j, d->cache, nullptr));
+    TRY(eval_block<T>(c, cv, d, j, d->cache, nullptr, ctx_ws(c)));
     hipLaunchKernelGGL(masked_copy_kernel, dim3(d->batch), dim3(256), 0, c->stream, cv->tokens, N, s, B, m.mask_id,
                        c->conf, c->tok, conf_cached, tok_cached);
     TRY(check_launch());
-    TRY(eval_block<T>(c, cv, d, j, DLLM_CACHE_NONE, nullptr));
+    TRY(eval_block<T>(c, cv, d, j, DLLM_CACHE_NONE, nullptr, ctx_ws(c)));
     hipLaunchKernelGGL(masked_copy_kernel, dim3(d->batch), dim3(256), 0, c->stream, cv->tokens, N, s, B, m.mask_id,
                        c->conf, c->tok, conf_fresh, tok_fresh);
     TRY(check_launch());
@@ -922,6 +975,16 @@ dllm_status dllm_init_weights(dllm_ctx** out, const dllm_model_cfg* cfg, const v
   dllm_ctx* c = new (std::nothrow) dllm_ctx();
   if (!c) return fail(DLLM_ERR_OOM, "host allocation failed");
   c->cfg = *cfg;
+  void* sp = nullptr;
+  dllm_status ss = hipGetDevice(&c->device) == hipSuccess ? scratch_address(c->device, &sp)
+                                                          : fail(DLLM_ERR_DEVICE, "hipGetDevice failed");
+  if (ss != DLLM_OK) {
+    std::string msg = g_err;
+    delete c;
+    g_err = msg;
+    return ss;
+  }
+  c->scratch_dev = static_cast<float*>(sp);
   c->stream = static_cast<hipStream_t>(hip_stream);
   c->bf16 = cfg->dtype == DLLM_BF16;
   c->esz = c->bf16 ? 2 : 4;
@@ -1056,15 +1119,16 @@ void dllm_set_device_limit(uint64_t bytes) { g_device_limit.store(bytes); }
 namespace {
 dllm_status block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg* cfg, int32_t block_idx,
                        int32_t* n_committed, int32_t* block_done, float* dbg_logits, float* dbg_conf, int32_t* dbg_tok,
-                       hipEvent_t* ev) {
+                       hipEvent_t* ev, const StepWs* ws_in = nullptr) {
   g_err.clear();
   if (!ctx || !canvas || !canvas->tokens) return fail(DLLM_ERR_ARG, "ctx, canvas and canvas->tokens must be non-NULL");
   TRY(validate_decode(ctx, cfg));
   if ((dbg_conf == nullptr) != (dbg_tok == nullptr)) return fail(DLLM_ERR_ARG, "dbg_conf and dbg_tok must both be set or both NULL");
   if (block_idx < 0 || block_idx >= cfg->gen_len / cfg->block_len) return fail(DLLM_ERR_ARG, "block_idx out of range");
   TRY(check_cache_ready(ctx, cfg, "dllm_block_step"));
-  return ctx->bf16 ? step_impl<f16_t>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok, ev)
-                   : step_impl<float>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok, ev);
+  const StepWs ws = ws_in ? *ws_in : ctx_ws(ctx);
+  return ctx->bf16 ? step_impl<f16_t>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok, ws, ev)
+                   : step_impl<float>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok, ws, ev);
 }
 
 // HIP events owned for the duration of one call
@@ -1092,6 +1156,45 @@ dllm_status dllm_block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decod
                             int32_t* n_committed, int32_t* block_done, float* dbg_logits, float* dbg_conf,
                             int32_t* dbg_tok) {
   return block_step(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok, nullptr);
+}
+
+dllm_status dllm_block_step_noalloc(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg* cfg, int32_t block_idx,
+                                    int32_t* n_committed, int32_t* block_done, float* dbg_logits, float* dbg_conf,
+                                    int32_t* dbg_tok) {
+  g_err.clear();
+  if (!ctx || !canvas || !canvas->tokens) return fail(DLLM_ERR_ARG, "ctx, canvas and canvas->tokens must be non-NULL");
+  TRY(validate_decode(ctx, cfg));
+  if (!ctx->scratch_dev) return fail(DLLM_ERR_DEVICE, "the static scratch of this device was not located");
+  // rows of the step's forward and of its LM head: both must take the
+  // skinny projections (<= 64 rows), which use no other workspace
+  const int N = cfg->prompt_len + cfg->gen_len;
+  const int s = cfg->prompt_len + std::max(0, std::min(block_idx, cfg->gen_len / cfg->block_len - 1)) * cfg->block_len;
+  const long nr = cfg->cache == DLLM_CACHE_NONE ? N : cfg->cache == DLLM_CACHE_PREFIX ? N - s : cfg->block_len;
+  const long rows = (long)cfg->batch * nr, head = (long)cfg->batch * cfg->block_len;
+  if (rows > 64 || head > 64)
+    return fail(DLLM_ERR_ARG, "dllm_block_step_noalloc serves steps of at most 64 recomputed rows (this one has " +
+                                  std::to_string(std::max(rows, head)) + "); use dllm_block_step");
+  // scratch layout: LM-head partials (max, sum, argmax), confidences and
+  // tokens, then the attention key-share partials in the rest
+  const size_t part = (size_t)ctx->n_vtiles * head;
+  const size_t fixed = 3 * part + 2 * (size_t)head;
+  const size_t total = kScratchBytes / sizeof(float);
+  const size_t attn_rec = (size_t)(ctx->cfg.head_dim / 32 * 16 + 2) * 64;   // one key share of one workgroup
+  if (fixed + attn_rec > total)
+    return fail(DLLM_ERR_ARG, "dllm_block_step_noalloc: the LM-head partials of " + std::to_string(head) + " rows x " +
+                                  std::to_string(ctx->cfg.vocab) + " vocabulary entries need " +
+                                  std::to_string((fixed + attn_rec) * sizeof(float)) + " bytes of scratch; it holds " +
+                                  std::to_string(kScratchBytes));
+  float* base = ctx->scratch_dev;
+  StepWs ws{};
+  ws.pmax = base;
+  ws.psum = base + part;
+  ws.parg = reinterpret_cast<int*>(base + 2 * part);
+  ws.conf = base + 3 * part;
+  ws.tok = reinterpret_cast<int*>(base + 3 * part + head);
+  ws.attn_ws = base + fixed;
+  ws.attn_ws_floats = total - fixed;
+  return block_step(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok, nullptr, &ws);
 }
 
 dllm_status dllm_staleness(dllm_ctx* ctx, const dllm_canvas* canvas, const dllm_decode_cfg* cfg, int32_t block_idx,

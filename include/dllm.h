@@ -244,6 +244,24 @@ dllm_status dllm_block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decod
                             int32_t block_idx, int32_t* n_committed, int32_t* block_done,
                             float* dbg_logits, float* dbg_conf, int32_t* dbg_tok);
 
+/* dllm_block_step for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same step, arguments, outputs and errors, with its per-step
+ * workspaces (LM-head partial (max, sum, argmax) per 16-entry vocabulary
+ * tile, confidences, tokens, attention key-share partials) in the library's
+ * static device scratch instead of the context's.  The scratch is one
+ * 16 MiB array per GPU, held until the process ends; every call on a GPU
+ * shares it and leaves its contents behind (each call writes every entry it
+ * reads before reading it, so nothing needs clearing), so calls that overlap
+ * on one GPU - from two streams, threads or contexts - race.  Serves steps
+ * whose forward and LM head cover at most 64 rows (batch x rows recomputed
+ * by the cache mode) and whose LM-head partials fit the scratch (vocab up to
+ * about 200k at 64 rows); any other step fails with DLLM_ERR_ARG before device
+ * work.  Allocates nothing (no hipMalloc, hipFree or allocating library call). */
+dllm_status dllm_block_step_noalloc(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg* cfg,
+                                    int32_t block_idx, int32_t* n_committed, int32_t* block_done,
+                                    float* dbg_logits, float* dbg_conf, int32_t* dbg_tok);
+
 /* Cached-vs-fresh diagnostics at the current canvas ([RN] sec. 14 and
  * Algorithm 4 steps 4-5: compare fresh and cached predictions at the commit
  * positions, and how far the cached K/V have drifted).  For block block_idx
