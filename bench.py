@@ -107,7 +107,16 @@ def main():
         hbm, mfma = L.dllm_probe_peaks(8 << 30)
         peaks = {"hbm_gbs": hbm, "mfma_f16_tflops": mfma,
                  "how": "library microkernels: streaming read of 8 GiB; 32x32x16 fp16 MFMA chains from registers"}
-        log(f"[bench] achievable: HBM read {hbm:.0f} GB/s, fp16 MFMA {mfma:.0f} TFLOP/s")
+        if shape.name == "llada8b":
+            # one cold streaming read of each step projection's weight bytes: the ceiling of a kernel that
+            # reads them once, launch ramp and drain included
+            d, f, v = shape.d_model, shape.d_ffn, shape.vocab
+            sizes = {"gateup": 2 * 2 * f * d, "qkv": 2 * 3 * d * d, "down": 2 * d * f, "oproj": 2 * d * d,
+                     "lmhead": 2 * v * d}
+            peaks["read_gbs_at_weight_bytes"] = {k: L.dllm_probe_read(b) for k, b in sizes.items()}
+            peaks["read_bytes"] = sizes
+        log(f"[bench] achievable: HBM read {hbm:.0f} GB/s, fp16 MFMA {mfma:.0f} TFLOP/s; streaming read at the "
+            f"projections' weight bytes: {peaks.get('read_gbs_at_weight_bytes')}")
     b16 = None if (args.no_b16 or args.probe) else workload("llada8b_p128_g128")
     max_batch = max(w.batch, b16.batch if b16 else 0)
     max_seq = max(w.seq_len, b16.seq_len if b16 else 0)
@@ -209,6 +218,9 @@ def main():
             out["step_hbm_fraction"]["vs_achievable"] = alg / (peaks["hbm_gbs"] * 1e9) / (ms_step / 1e3)
     if peaks:
         out["achievable"] = peaks
+        at = peaks.get("read_gbs_at_weight_bytes", {}).get(dom)
+        if at and roof["unit"] == "GB/s":
+            roof["frac_of_read_at_same_bytes"] = roof["achieved"] / at
     if b16 is not None:
         out["b16_projection_mfma_fraction"] = b16_projections(eng, b16, L)
     eng.close()

@@ -20,7 +20,8 @@ RULE = {"threshold": 0, "factor": 1, "topk": 2, "budget": 3, "steps": 4}
 
 SYMBOLS = ("dllm_init_weights", "dllm_refresh_cache", "dllm_block_step", "dllm_block_step_noalloc",
            "dllm_staleness", "dllm_begin_decode",
-           "dllm_decode", "dllm_set_timing", "dllm_get_timing", "dllm_probe_peaks", "dllm_set_device_limit",
+           "dllm_decode", "dllm_set_timing", "dllm_get_timing", "dllm_probe_peaks", "dllm_probe_read",
+           "dllm_set_device_limit",
            "dllm_destroy", "dllm_last_error")
 KERNEL_CLASSES = ("embed", "rmsnorm", "qkv", "attn", "oproj", "gateup", "down", "lmhead", "merge",
                   "select")
@@ -89,6 +90,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.dllm_begin_decode.restype = C.c_int
     lib.dllm_probe_peaks.argtypes = [C.c_uint64, C.POINTER(C.c_double), C.POINTER(C.c_double)]
     lib.dllm_probe_peaks.restype = C.c_int
+    lib.dllm_probe_read.argtypes = [C.c_uint64, C.POINTER(C.c_double)]
+    lib.dllm_probe_read.restype = C.c_int
     lib.dllm_decode.argtypes = [P, C.POINTER(Canvas), C.POINTER(DecodeCfg), C.POINTER(Stats)]
     lib.dllm_decode.restype = C.c_int
     lib.dllm_set_timing.argtypes = [P, C.c_uint32, C.c_uint32]
@@ -158,6 +161,13 @@ def dllm_probe_peaks(nbytes: int = 8 << 30):
     hbm, mfma = C.c_double(0.0), C.c_double(0.0)
     check(load().dllm_probe_peaks(C.c_uint64(nbytes), C.byref(hbm), C.byref(mfma)))
     return hbm.value, mfma.value
+
+
+def dllm_probe_read(nbytes: int) -> float:
+    """Best streaming-read GB/s of device 0 for one read of `nbytes` bytes from HBM."""
+    g = C.c_double(0.0)
+    check(load().dllm_probe_read(C.c_uint64(nbytes), C.byref(g)))
+    return g.value
 
 
 def dllm_set_timing(ctx: int, classes, sample_every: int = 1) -> None:

@@ -354,6 +354,17 @@ dllm_status dllm_get_timing(dllm_ctx* ctx, dllm_kernel_time* out, int32_t reset)
  * Errors: DLLM_ERR_ARG (bytes < 1 MiB), DLLM_ERR_OOM, DLLM_ERR_DEVICE. */
 dllm_status dllm_probe_peaks(uint64_t bytes, double* hbm_gbs, double* mfma_f16_tflops);
 
+/* Streaming-read rate at a given size: the best GB/s of hbm_read_kernel
+ * reading one `bytes`-byte buffer (one launch, kernel duration from its
+ * dispatch packet; 256, 512 and 1024 workgroups tried), the buffer rotating
+ * over copies that together exceed the memory-side cache, so every read comes
+ * from HBM.  At the size of one projection's weights this is the ceiling of
+ * a kernel that streams them once, ramp-up and drain included, which a read
+ * of gigabytes (dllm_probe_peaks) hides.  Allocates its buffers (up to 32 x
+ * bytes, at least 1 GiB) for the duration of the call.
+ * Errors: DLLM_ERR_ARG (bytes < 1 MiB or gbs NULL), DLLM_ERR_OOM, DLLM_ERR_DEVICE. */
+dllm_status dllm_probe_read(uint64_t bytes, double* gbs);
+
 /* Process-wide cap on the device memory a context may hold: dllm_init_weights
  * fails with DLLM_ERR_OOM, before allocating past it, when the packed weights,
  * KV cache and workspaces of the requested shape exceed `bytes`, and
