@@ -53,3 +53,34 @@ def test_null_arguments_rejected():
     assert lib.dllm_block_step(None, C.byref(cv), C.byref(cfg), 0, None, None, None, None, None) == L.ERR_ARG
     assert lib.dllm_init_weights(None, C.byref(_tiny_cfg()), None, None) == L.ERR_ARG
     lib.dllm_destroy(None)
+
+
+def test_header_compiles_as_plain_c(tmp_path):
+    """include/dllm.h is a C header: a C99 translation unit that includes it
+    and takes the address of every declared function compiles warning-free."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    names = _declared()
+    src = tmp_path / "use_header.c"
+    src.write_text('#include "dllm.h"\n#include <stddef.h>\n'
+                   "typedef void (*fn_t)(void);\n"
+                   "fn_t dllm_symbols[] = {\n" + ",\n".join(f"  (fn_t){n}" for n in names) + "\n};\n"
+                   "int dllm_sizes_ok(void) {\n"
+                   "  return sizeof(dllm_model_cfg) == 12 * 4 && sizeof(dllm_decode_cfg) == 10 * 4 &&\n"
+                   "         sizeof(dllm_canvas) == 4 * sizeof(void*) && sizeof(dllm_stats) == 8 * 8;\n}\n")
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.dirname(HDR),
+                        "-c", str(src), "-o", str(tmp_path / "use_header.o")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_struct_layouts_match_the_binding():
+    """The ctypes structures mirror the header's structs field for field."""
+    assert C.sizeof(L.ModelCfg) == 12 * 4
+    assert C.sizeof(L.DecodeCfg) == 10 * 4
+    assert C.sizeof(L.Canvas) == 4 * C.sizeof(C.c_void_p)
+    assert C.sizeof(L.Stats) == 8 * 8
+    assert [f for f, _ in L.Stats._fields_] == ["steps", "refreshes", "committed", "max_seq_steps", "ms_total",
+                                                "ms_refresh", "ms_step", "ms_select"]
