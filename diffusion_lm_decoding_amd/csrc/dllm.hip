@@ -3,6 +3,7 @@
 // and the host block loop (Fast-dLLM reading notes, Algorithm 1).
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <algorithm>
 #include <atomic>
@@ -45,6 +46,20 @@ dllm_status fail(dllm_status s, const std::string& msg) {
     dllm_status s_ = (call);              \
     if (s_ != DLLM_OK) return s_;         \
   } while (0)
+
+// Host-side roctx range around a library call or a phase of dllm_decode
+// (visible under rocprofv3 --marker-trace; no-ops when no tool is attached).
+struct Range {
+  explicit Range(const char* name) { roctxRangePushA(name); }
+  Range(const char* fmt, int v) {
+    char buf[64];
+    std::snprintf(buf, sizeof(buf), fmt, v);
+    roctxRangePushA(buf);
+  }
+  ~Range() { roctxRangePop(); }
+  Range(const Range&) = delete;
+  Range& operator=(const Range&) = delete;
+};
 
 constexpr int kMaxBlock = 256;      // select/commit handles a block in one workgroup
 
@@ -1135,6 +1150,7 @@ void dllm_destroy(dllm_ctx* ctx) {
 
 dllm_status dllm_refresh_cache(dllm_ctx* ctx, const dllm_canvas* canvas, const dllm_decode_cfg* cfg, int32_t block_idx) {
   g_err.clear();
+  const Range range("dllm_refresh_cache");
   if (!ctx || !canvas || !canvas->tokens) return fail(DLLM_ERR_ARG, "ctx, canvas and canvas->tokens must be non-NULL");
   TRY(validate_decode(ctx, cfg));
   const bool commit_pass = cfg->cache == DLLM_CACHE_BLOCK_CAUSAL && block_idx >= 0;
@@ -1161,6 +1177,7 @@ dllm_status block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg
                        int32_t* n_committed, int32_t* block_done, float* dbg_logits, float* dbg_conf, int32_t* dbg_tok,
                        hipEvent_t* ev, const StepWs* ws_in = nullptr) {
   g_err.clear();
+  const Range range("dllm_block_step");
   if (!ctx || !canvas || !canvas->tokens) return fail(DLLM_ERR_ARG, "ctx, canvas and canvas->tokens must be non-NULL");
   TRY(validate_decode(ctx, cfg));
   if ((dbg_conf == nullptr) != (dbg_tok == nullptr)) return fail(DLLM_ERR_ARG, "dbg_conf and dbg_tok must both be set or both NULL");
@@ -1186,6 +1203,28 @@ struct Events {
     float v = 0.f;
     if (hipEventElapsedTime(&v, e[a], e[b]) != hipSuccess) *st = fail(DLLM_ERR_DEVICE, "hipEventElapsedTime failed");
     return v;
+  }
+};
+
+// DLLM_TRACE=<path>: dllm_decode appends one JSON line per cache pass, per
+// step and per decode to that file (opened per call, closed on return).
+struct TraceFile {
+  std::FILE* f = nullptr;
+  dllm_status open() {
+    const char* path = std::getenv("DLLM_TRACE");
+    if (!path || !*path) return DLLM_OK;
+    f = std::fopen(path, "a");
+    if (!f) return fail(DLLM_ERR_ARG, std::string("DLLM_TRACE: cannot open ") + path + " for appending");
+    return DLLM_OK;
+  }
+  ~TraceFile() {
+    if (f) std::fclose(f);
+  }
+  template <typename V>
+  void list(const char* key, const V& v, int n) {
+    std::fprintf(f, ",\"%s\":[", key);
+    for (int i = 0; i < n; ++i) std::fprintf(f, i ? ",%d" : "%d", (int)v[i]);
+    std::fputc(']', f);
   }
 };
 }  // namespace
@@ -1280,6 +1319,9 @@ dllm_status dllm_begin_decode(dllm_ctx* ctx, const dllm_canvas* canvas, const dl
 dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg* cfg, dllm_stats* stats) {
   const auto t_start = std::chrono::steady_clock::now();
   TRY(dllm_begin_decode(ctx, canvas, cfg));
+  const Range decode_range("dllm_decode");
+  TraceFile tr;
+  TRY(tr.open());
 
   // e[0], e[1]: around a cache pass; e[2..4]: a step's forward / selection
   // split, taken on every kSplitEvery-th step only (each event pair lengthens
@@ -1294,38 +1336,55 @@ dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cf
   std::vector<int64_t> seq_steps(cfg->batch, 0);
   const bool steps_rule = cfg->rule == DLLM_RULE_STEPS;
   const int max_in_block = steps_rule ? cfg->k : cfg->block_len;
-  auto timed_refresh = [&](int blk) -> dllm_status {
+  // block: the answer block being decoded (-1 before the first)
+  auto timed_refresh = [&](int blk, int block, int in_block) -> dllm_status {
     HIPCHK(hipEventRecord(ev.e[0], ctx->stream));
     TRY(dllm_refresh_cache(ctx, canvas, cfg, blk));
     HIPCHK(hipEventRecord(ev.e[1], ctx->stream));
     HIPCHK(hipEventSynchronize(ev.e[1]));
     dllm_status es = DLLM_OK;
-    ms_refresh += ev.ms(0, 1, &es);
+    const double ms = ev.ms(0, 1, &es);
+    ms_refresh += ms;
     ++refreshes;
+    if (tr.f)
+      std::fprintf(tr.f, "{\"event\":\"refresh\",\"block\":%d,\"in_block\":%d,\"pass\":%d,\"ms\":%.4f}\n",
+                   block, in_block, blk, ms);
     return es;
   };
   dllm_status st = DLLM_OK;
   const int nb = cfg->gen_len / cfg->block_len;
   const bool bc = cfg->cache == DLLM_CACHE_BLOCK_CAUSAL;
   const bool cached = cfg->cache == DLLM_CACHE_PREFIX || cfg->cache == DLLM_CACHE_DUAL;
-  if (bc) st = timed_refresh(-1);
+  if (bc) st = timed_refresh(-1, -1, 0);
   for (int j = 0; st == DLLM_OK && j < nb; ++j) {
-    if (cached) st = timed_refresh(0);
+    const Range block_range("block %d", j);
+    if (cached) st = timed_refresh(0, j, 0);
     int in_block = 0;
     std::fill(was_done.begin(), was_done.end(), 0);
     while (st == DLLM_OK) {
       if (cached && cfg->refresh_every > 0 && in_block > 0 && in_block % cfg->refresh_every == 0) {
-        st = timed_refresh(0);
+        st = timed_refresh(0, j, in_block);
         if (st != DLLM_OK) break;
       }
       hipEvent_t* step_ev = (stats && steps % kSplitEvery == 0) ? ev.e + 2 : nullptr;
       st = block_step(ctx, canvas, cfg, j, nc.data(), done.data(), nullptr, nullptr, nullptr, step_ev);
       if (st != DLLM_OK) break;
+      double ms_fwd = -1.0, ms_sel = -1.0;
       if (step_ev) {   // the step returned after its status readback: the events are complete
-        ms_step += ev.ms(2, 3, &st);
-        ms_select += ev.ms(3, 4, &st);
+        ms_fwd = ev.ms(2, 3, &st);
+        ms_sel = ev.ms(3, 4, &st);
+        ms_step += ms_fwd;
+        ms_select += ms_sel;
         ++split_steps;
         if (st != DLLM_OK) break;
+      }
+      if (tr.f) {
+        std::fprintf(tr.f, "{\"event\":\"step\",\"block\":%d,\"in_block\":%d,\"step\":%lld", j, in_block,
+                     (long long)steps);
+        tr.list("committed", nc, cfg->batch);
+        tr.list("done", done, cfg->batch);
+        if (step_ev) std::fprintf(tr.f, ",\"ms_forward\":%.4f,\"ms_select\":%.4f", ms_fwd, ms_sel);
+        std::fputs("}\n", tr.f);
       }
       ++steps;
       ++in_block;
@@ -1346,9 +1405,12 @@ dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cf
         break;
       }
     }
-    if (st == DLLM_OK && bc) st = timed_refresh(j);
+    if (st == DLLM_OK && bc) st = timed_refresh(j, j, in_block);
   }
   if (st != DLLM_OK) return st;
+  if (tr.f)
+    std::fprintf(tr.f, "{\"event\":\"decode\",\"steps\":%lld,\"refreshes\":%lld,\"committed\":%lld}\n",
+                 (long long)steps, (long long)refreshes, (long long)committed);
   if (stats) {
     stats->steps = steps;
     stats->refreshes = refreshes;

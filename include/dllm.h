@@ -299,7 +299,16 @@ dllm_status dllm_begin_decode(dllm_ctx* ctx, const dllm_canvas* canvas, const dl
  * block holds no mask in any sequence (lock-step over the batch; finished
  * sequences commit nothing).  No refresh follows the last block.
  *   stats: host output or NULL.
- * Errors: DLLM_ERR_ARG, DLLM_ERR_STATE (a step of a rule other than STEPS
+ * Tracing: with the environment variable DLLM_TRACE set to a path, one JSON
+ *   line is appended there per cache pass ({"event":"refresh", block,
+ *   in_block, pass = block_idx given to dllm_refresh_cache, ms}), per step
+ *   ({"event":"step", block, in_block, step, committed[batch], done[batch],
+ *   and on every 8th step ms_forward / ms_select}) and per decode
+ *   ({"event":"decode", steps, refreshes, committed}).  dllm_decode, each
+ *   block, dllm_refresh_cache and dllm_block_step push roctx ranges
+ *   (rocprofv3 --marker-trace).
+ * Errors: DLLM_ERR_ARG (also: DLLM_TRACE names a file that cannot be opened
+ *   for appending), DLLM_ERR_STATE (a step of a rule other than STEPS
  *   committed nothing while masks remained, or a block outlived its step
  *   bound), DLLM_ERR_NUMERIC, DLLM_ERR_DEVICE. */
 dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg* cfg,

@@ -6,6 +6,8 @@ DLLM_ERR_NUMERIC with the canvas unchanged; and the decode statistics split
 the device time as eq. (15) of the reading notes does (steps, refreshes,
 selection).  Every error is raised from the host before or after complete
 kernels; nothing here faults or stalls the GPU."""
+import json
+
 import numpy as np
 import pytest
 import torch
@@ -132,3 +134,35 @@ def test_stats_split_device_time(eng32):
     assert st.ms_step > 0 and st.ms_select > 0 and st.ms_refresh > 0
     assert st.ms_step + st.ms_select + st.ms_refresh <= st.ms_total
     assert st.refreshes == 4 and st.committed == 64
+
+
+def test_trace_log_matches_stats(eng32, tmp_path, monkeypatch):
+    """DLLM_TRACE: one line per cache pass and per step, whose counts add up
+    to the decode's statistics; an unopenable path is an argument error."""
+    from diffusion_lm_decoding_amd import _lib as L
+    from diffusion_lm_decoding_amd.engine import Engine
+    pr, t, a = _inputs(batch=2)
+    cfg = Engine.decode_cfg(2, 32, 64, 16)
+    path = tmp_path / "trace.jsonl"
+    monkeypatch.setenv("DLLM_TRACE", str(path))
+    cv = eng32.canvas(pr, t, a, 64)
+    st = eng32.decode(cv, cfg)
+    lines = [json.loads(x) for x in path.read_text().splitlines()]
+    steps = [x for x in lines if x["event"] == "step"]
+    refreshes = [x for x in lines if x["event"] == "refresh"]
+    assert lines[-1] == {"event": "decode", "steps": st.steps, "refreshes": st.refreshes, "committed": st.committed}
+    assert len(steps) == st.steps and len(refreshes) == st.refreshes == 4
+    assert sum(sum(x["committed"]) for x in steps) == st.committed == 128
+    assert [x["step"] for x in steps] == list(range(st.steps))
+    for j in range(4):
+        blk = [x for x in steps if x["block"] == j]
+        assert [x["in_block"] for x in blk] == list(range(len(blk)))
+        assert blk[-1]["done"] == [1, 1]
+        assert sum(sum(x["committed"]) for x in blk) == 2 * 16
+    assert all(("ms_forward" in x) == (x["step"] % 8 == 0) for x in steps)
+    assert all(x["ms"] > 0 for x in refreshes)
+    monkeypatch.setenv("DLLM_TRACE", str(tmp_path / "no_such_dir" / "trace.jsonl"))
+    cv = eng32.canvas(pr, t, a, 64)
+    with pytest.raises(L.DllmError) as e:
+        eng32.decode(cv, cfg)
+    assert e.value.status == L.ERR_ARG and "DLLM_TRACE" in str(e.value)
