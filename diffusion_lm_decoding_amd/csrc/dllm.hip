@@ -157,6 +157,7 @@ struct dllm_ctx {
   size_t gemm_part_floats = 0;
   float* attn_ws = nullptr;
   size_t attn_ws_floats = 0;
+  int head_group = 1;         // vocabulary tiles per LM-head partial of the last head launch
 
   // one device status block [ncommit(max_batch) | done(max_batch) | err(4)],
   // read back by a single copy per step into h_pin (same layout)
@@ -340,8 +341,15 @@ double gemm_out_bytes(int cls, int M, int N, int es) {
 // tiles; NT = 2 when that still leaves a multiple of 256 workgroups or very
 // many of them.  Larger M goes to the LDS-tiled kernel.
 template <typename T, int MT, int NT, int U, class Epi>
-dllm_status launch_skinny(dllm_ctx* c, const Timed& tm, const GemmArgs& a, const Epi& epi) {
+dllm_status launch_skinny(dllm_ctx* c, const Timed& tm, const GemmArgs& a, const Epi& epi_in) {
   const unsigned grid = (unsigned)((a.n_tiles / NT) * a.m_groups);
+  Epi epi = epi_in;
+  if constexpr (GroupMerge<Epi>::value) {
+    // the LM head's workgroups combine their NT vocabulary tiles (one
+    // partial per row and workgroup for the merge kernel)
+    epi.group = NT;
+    c->head_group = NT;
+  }
   if (grid <= 256)
     hipExtLaunchKernelGGL((gemm_skinny_kernel<T, MT, NT, 8, Epi, U, true>), dim3(grid), dim3(512), 0, c->stream,
                           tm.a, tm.b, 0, a, epi);
@@ -482,6 +490,8 @@ dllm_status launch_gemm(dllm_ctx* c, int cls, const void* X, const void* W, int 
     if (a.m_tiles == 1) TRY((launch_skinny_nt<T, 1>(c, tm, a, epi)));
     else if (a.m_tiles == 2) TRY((launch_skinny_nt<T, 2>(c, tm, a, epi)));
     else TRY((launch_skinny_nt<T, 4>(c, tm, a, epi)));
+    // the LM head writes one partial per (row, head_group tiles)
+    if (cls == DLLM_K_LMHEAD) tm.bytes -= 12.0 * M * (N / 16) * (1.0 - 1.0 / c->head_group);
     return tm.done();
   }
   Timed tm(c, cls, bytes, 2.0 * M * N * K);
@@ -721,12 +731,14 @@ dllm_status eval_block(dllm_ctx* c, const dllm_canvas* cv, const dllm_decode_cfg
   TRY(check_launch());
   EpiLMHead eh{HR, B, d->gen_len, s - d->prompt_len, cv->bias_target, cv->bias_alpha, m.mask_id, m.vocab,
                c->n_vtiles, ws.pmax, ws.psum, ws.parg, dbg_logits, rowmap, count};
+  c->head_group = 1;   // the skinny launch sets its n-tiles per workgroup
   TRY(launch_gemm<T>(c, DLLM_K_LMHEAD, compact ? c->xc : c->xh, c->wlm, HR, m.vocab, m.d_model, eh,
                      compact ? c->ssq_c : c->ssq_head, HR, count));
   if (after_head) HIPCHK(hipEventRecord(after_head, c->stream));
-  Timed tm(c, DLLM_K_MERGE, 12.0 * c->n_vtiles * HR + 8.0 * HR, 3.0 * c->n_vtiles * HR);
+  const int n_parts = c->n_vtiles / c->head_group;
+  Timed tm(c, DLLM_K_MERGE, 12.0 * n_parts * HR + 8.0 * HR, 3.0 * n_parts * HR);
   hipLaunchKernelGGL(lm_merge_kernel, dim3(HR), dim3(kMergeThreads), 0, c->stream, ws.pmax, ws.psum, ws.parg,
-                     c->n_vtiles, HR, ws.conf, ws.tok, c->d_err, rowmap, count);
+                     n_parts, HR, ws.conf, ws.tok, c->d_err, rowmap, count);
   return tm.done();
 }
 

@@ -199,8 +199,12 @@ struct EpiSwiGLU {
 // LM head: planted bias, mask_id excluded, then per (16-entry vocab tile,
 // row) the (max, argmax, sum exp(l - max)) that the merge kernel combines.
 // Ties keep the lowest vocabulary index.  Logits never leave registers unless
-// a debug buffer is given.
+// a debug buffer is given.  With group > 1 (the skinny kernel, group = its
+// n-tiles per workgroup) a workgroup first combines its group consecutive
+// tiles in LDS, in tile order, and stores one partial per (row, group): the
+// partial arrays are [M][n_tiles / group].
 struct EpiLMHead {
+  static constexpr bool kGroupMerge = true;
   int M;                  // head rows = batch * block_len
   int blk;                // block_len
   int gen_len, gen_off;   // row m -> bias index (m/blk)*gen_len + gen_off + m%blk
@@ -208,7 +212,7 @@ struct EpiLMHead {
   const float* alpha;
   int mask_id, vocab;
   int n_tiles;            // vocab / 16
-  float* pmax;            // [M][n_tiles]: each row's partials contiguous for the merge
+  float* pmax;            // [M][n_tiles / group]: each row's partials contiguous for the merge
   float* psum;
   int* parg;
   float* dbg;             // [M][vocab] (block rows) or null
@@ -216,9 +220,13 @@ struct EpiLMHead {
   // are not written
   const int* rowmap;
   const int* count;
-  __device__ void operator()(int nt, int mt, const f32x4& acc, int lane) const {
+  int group = 1;
+  __device__ bool row_valid(int m) const { return m < (count ? *count : M); }
+  // (max, sum exp(l - max), argmax) of tile nt for row mt * 16 + lane % 16,
+  // complete in lanes 0..15
+  __device__ void reduce(int nt, int mt, const f32x4& acc, int lane, float& mx, float& s, int& am) const {
     const int m = mt * 16 + (lane & 15);
-    const bool valid = m < (count ? *count : M);
+    const bool valid = row_valid(m);
     const int br = rowmap ? rowmap[valid ? m : 0] : m;   // block row
     int tgt = -1;
     float al = 0.f;
@@ -228,8 +236,8 @@ struct EpiLMHead {
       al = alpha[bi];
     }
     float v[4];
-    float mx = -INFINITY;
-    int am = 0x7fffffff;
+    mx = -INFINITY;
+    am = 0x7fffffff;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int voc = nt * 16 + acc16_row(r, lane);
@@ -246,18 +254,29 @@ struct EpiLMHead {
       const int oam = __shfl_xor(am, o);
       if (omx > mx || (omx == mx && oam < am)) { mx = omx; am = oam; }
     }
-    float s = 0.f;
+    s = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) s += expf(v[r] - mx);
     s += __shfl_xor(s, 16);
     s += __shfl_xor(s, 32);
-    if (valid && lane < 16) {
-      pmax[(size_t)m * n_tiles + nt] = mx;
-      psum[(size_t)m * n_tiles + nt] = s;
-      parg[(size_t)m * n_tiles + nt] = am;
-    }
+  }
+  __device__ void store(int part, int m, float mx, float s, int am) const {
+    const size_t n_parts = n_tiles / group;
+    pmax[(size_t)m * n_parts + part] = mx;
+    psum[(size_t)m * n_parts + part] = s;
+    parg[(size_t)m * n_parts + part] = am;
+  }
+  __device__ void operator()(int nt, int mt, const f32x4& acc, int lane) const {
+    float mx, s;
+    int am;
+    reduce(nt, mt, acc, lane, mx, s, am);
+    const int m = mt * 16 + (lane & 15);
+    if (row_valid(m) && lane < 16) store(nt, m, mx, s, am);
   }
 };
+
+template <class E, class = void> struct GroupMerge : std::false_type {};
+template <class E> struct GroupMerge<E, std::void_t<decltype(E::kGroupMerge)>> : std::true_type {};
 
 // ---------------------------------------------------------------------------
 struct GemmArgs {
@@ -440,6 +459,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmArgs a, Epi ep
 #pragma unroll
       for (int r = 0; r < 4; ++r) red[wave][(j * MT + i) * 4 + r][lane] = acc[j][i][r];
   __syncthreads();
+  // LM head with group = NT: the tile reductions meet in LDS and one wave per
+  // m-tile combines the workgroup's NT tiles in tile order
+  constexpr bool kGroup = GroupMerge<Epi>::value;
+  __shared__ float g_mx[kGroup ? MT : 1][kGroup ? NT : 1][16], g_s[kGroup ? MT : 1][kGroup ? NT : 1][16];
+  __shared__ int g_am[kGroup ? MT : 1][kGroup ? NT : 1][16];
+  bool grouped = false;
+  if constexpr (kGroup) grouped = epi.group == NT && NT > 1;
   for (int t = wave; t < TILES; t += NW) {
     const int j = t / MT, i = t % MT;
     if (i >= nmt) continue;
@@ -454,7 +480,42 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmArgs a, Epi ep
       for (int w = 0; w < NW; ++w) s2 += ssq_red[w][i][lane & 15];
       v *= 1.0f / sqrtf(s2 * a.inv_k + a.eps);
     }
+    if constexpr (kGroup) {
+      if (grouped) {
+        float mx, s;
+        int am;
+        epi.reduce(nt0 + j, mt0 + i, v, lane, mx, s, am);
+        if (lane < 16) {
+          g_mx[i][j][lane] = mx;
+          g_s[i][j][lane] = s;
+          g_am[i][j][lane] = am;
+        }
+        continue;
+      }
+    }
     epi(nt0 + j, mt0 + i, v, lane);
+  }
+  if constexpr (kGroup) {
+    if (grouped) {
+      __syncthreads();
+      const int m = (mt0 + wave) * 16 + lane;
+      if (wave < nmt && lane < 16 && epi.row_valid(m)) {
+        float mx = -INFINITY;
+        int am = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const float x = g_mx[wave][j][lane];
+          const int ax = g_am[wave][j][lane];
+          if (x > mx || (x == mx && ax < am)) { mx = x; am = ax; }
+        }
+        float s = 0.f;
+        if (mx != -INFINITY) {
+#pragma unroll
+          for (int j = 0; j < NT; ++j) s += g_s[wave][j][lane] * expf(g_mx[wave][j][lane] - mx);
+        }
+        epi.store(nt0 / NT, m, mx, s, am);
+      }
+    }
   }
 }
 

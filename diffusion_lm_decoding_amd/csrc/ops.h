@@ -83,9 +83,10 @@ __global__ __launch_bounds__(256) void embed_kernel(const int* tokens, int seq_l
   }
 }
 
-// ---- LM-head merge: per row, combine the vocab-tile partials ---------------
+// ---- LM-head merge: per row, combine the vocabulary partials --------------
 // max and argmax (lowest index among equal maxima), then
-// S = sum_t s_t exp(m_t - max); confidence = 1 / S.  Partials are [M][n_tiles];
+// S = sum_t s_t exp(m_t - max); confidence = 1 / S.  Partials are [M][n_tiles]
+// (n_tiles: partials per row, each covering consecutive vocabulary tiles);
 // one workgroup of kMergeThreads per row.  Each thread keeps its first
 // kMergePer tiles in registers (every load issued before the first use), so
 // the second pass re-reads memory only for vocabularies beyond

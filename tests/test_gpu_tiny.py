@@ -246,3 +246,31 @@ def test_nan_bias_reports_numeric_error_and_leaves_canvas(engines):
         eng.step(cv, cfg, 0)
     assert e.value.status == L.ERR_NUMERIC
     assert torch.equal(before, cv.tokens)
+
+
+@pytest.mark.parametrize("vocab", [8192, 65536])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_grouped_head_partials_lockstep(vocab, dtype):
+    """Vocabularies whose LM-head launch puts 2 (8192) or 4 (65536) vocabulary
+    tiles in a workgroup: the workgroup combines its tiles' (max, sum,
+    argmax) before the merge kernel.  Lock-step against the oracle."""
+    from diffusion_lm_decoding_amd.engine import Engine
+    shape = TINY.__class__(**{**TINY.__dict__, "vocab": vocab, "mask_id": vocab - 1, "dtype": dtype,
+                              "name": f"tiny_v{vocab}_{dtype}"})
+    w = gen_weights(shape, seed=5, gain_jitter=0.1)
+    eng = Engine(shape, w, max_batch=2, max_seq=96)
+    om = OracleModel(shape, w)
+    pr = gen_prompt(shape, 2, 32, 71)
+    t, a = gen_bias(shape, 2, 64, 72, 16.0)
+    cfg = Engine.decode_cfg(2, 32, 64, 16, cache="dual", rule="threshold", tau=0.9)
+    cv = eng.canvas(pr, t, a, 64)
+    fp32 = dtype == "f32"
+    rep = replay(eng, cv, cfg, om, pr, t, a, "dual", "threshold", tol=Tol(fp32=fp32), seq=1, tau=0.9)
+    print(f"vocab {vocab} {dtype}: {rep.summary()}", flush=True)
+    eng.close()
+    assert not rep.bad, rep.bad[:5]
+    assert rep.steps >= 4
+    if fp32:
+        assert rep.max_logit_err < 1e-4
+    else:
+        assert rep.max_logit_err < 5e-2 and rep.max_conf_err < 1e-2
