@@ -160,7 +160,7 @@ struct dllm_ctx {
   int head_group = 1;         // vocabulary tiles per LM-head partial of the last head launch
 
   // one device status block [ncommit(max_batch) | done(max_batch) | err(4)],
-  // read back by a single copy per step into h_pin (same layout)
+  // mirrored into h_pin (same layout) by the select/commit kernel
   int* d_stat = nullptr;
   int* d_err = nullptr;       // d_stat + 2 max_batch: [0] numeric error, [1] canvas check
   int* d_ncommit = nullptr;   // d_stat
@@ -630,7 +630,7 @@ dllm_status forward(dllm_ctx* c, const Fwd& f) {
   using Tin = typename InType<T>::type;
   hipLaunchKernelGGL((embed_kernel<Tin, T>), dim3(M), dim3(256), 0, c->stream, f.tokens, f.seq_len, g,
                      static_cast<const Tin*>(c->emb), d, m.vocab, c->x, c->g_attn[0], static_cast<T*>(c->xin),
-                     c->ssq);
+                     c->ssq, f.head_blk > 0 ? c->d_err : nullptr);
   TRY(te.done());
   T* xin = static_cast<T*>(c->xin);
   // normalised input of the next projection over all M rows
@@ -720,7 +720,6 @@ dllm_status eval_block(dllm_ctx* c, const dllm_canvas* cv, const dllm_decode_cfg
   const bool compact = HR > 64 && HR <= 32 * 1024;
   const int* rowmap = compact ? c->head_rowmap : nullptr;
   const int* count = compact ? c->head_count : nullptr;
-  hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, c->stream, c->d_err, 2, 0);
   if (compact) {
     hipLaunchKernelGGL(head_rows_kernel, dim3(1), dim3(1024), 0, c->stream, cv->tokens, f.seq_len, s, B, HR,
                        m.mask_id, c->head_rowmap, c->head_count);
@@ -779,6 +778,8 @@ dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, in
   sa.ncommit = c->d_ncommit;
   sa.done = c->d_done;
   sa.err = c->d_err;
+  sa.host_stat = c->h_pin;
+  sa.max_batch = c->cfg.max_batch;
   sa.dbg_conf = dbg_conf;
   sa.dbg_tok = dbg_tok;
   {
@@ -787,8 +788,8 @@ dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, in
     TRY(tm.done());
   }
   if (ev) HIPCHK(hipEventRecord(ev[2], c->stream));
+  // select/commit wrote the status block into pinned host memory
   const int mb = c->cfg.max_batch;
-  HIPCHK(hipMemcpyAsync(c->h_pin, c->d_stat, (2 * (size_t)mb + 1) * sizeof(int), hipMemcpyDeviceToHost, c->stream));
   HIPCHK(hipStreamSynchronize(c->stream));
   if (c->h_pin[2 * mb]) return fail(DLLM_ERR_NUMERIC, "non-finite logits or confidence in the LM head");
   for (int b = 0; b < d->batch; ++b) {

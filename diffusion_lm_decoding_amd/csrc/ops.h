@@ -34,8 +34,10 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
 template <typename Tin, typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const int* tokens, int seq_len, RowGeom g,
                                                     const Tin* emb, int d, int vocab, float* x,
-                                                    const float* gain, T* xg, float* ssq) {
+                                                    const float* gain, T* xg, float* ssq, int* err_reset) {
   const int m = blockIdx.x;
+  // a forward that ends in the LM head starts the step's error flags at zero
+  if (err_reset && m == 0 && threadIdx.x < 2) err_reset[threadIdx.x] = 0;
   const int b = m / g.nr, pos = g.row_start + m % g.nr;
   const int tok = min(max(tokens[(size_t)b * seq_len + pos], 0), vocab - 1);
   const Tin* e = emb + (size_t)tok * d;
@@ -219,6 +221,11 @@ struct SelectArgs {
   int* ncommit;         // [batch]
   int* done;            // [batch]
   const int* err;       // nonzero: commit nothing
+  // pinned host status block [ncommit[max_batch], done[max_batch], err]:
+  // written with system-scope stores, read by the host after the stream
+  // synchronises (no copy back)
+  int* host_stat;
+  int max_batch;
   float* dbg_conf;      // [batch*blk] or null
   int* dbg_tok;
 };
@@ -296,8 +303,12 @@ __global__ __launch_bounds__(256) void select_commit_kernel(SelectArgs a) {
   }
   const int cnt = (int)block_sum<256>(sel ? 1.f : 0.f, red);
   if (i == 0) {
+    const int dn = (n_masked - cnt == 0) ? 1 : 0;
     a.ncommit[b] = cnt;
-    a.done[b] = (n_masked - cnt == 0) ? 1 : 0;
+    a.done[b] = dn;
+    __hip_atomic_store(a.host_stat + b, cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(a.host_stat + a.max_batch + b, dn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (b == 0) __hip_atomic_store(a.host_stat + 2 * a.max_batch, *a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     if (n_masked > 0 && !*a.err) {
       a.step_ctr[b] = step + 1;
       a.blk_id[b] = a.block_idx;
