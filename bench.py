@@ -115,8 +115,18 @@ def main():
                      "lmhead": 2 * v * d}
             peaks["read_gbs_at_weight_bytes"] = {k: L.dllm_probe_read(b) for k, b in sizes.items()}
             peaks["read_bytes"] = sizes
+        # what a large-M projection's main loop leaves of the MFMA rate: the same MFMA stream with the LDS
+        # reads (8 KiB per 16 MFMAs: a 128x128 wave tile) and DMA copies into LDS (4 KiB per wave per 16
+        # MFMAs: a 256x256 workgroup tile; 2: half of that) beside it, at one and two waves per SIMD
+        mix = {}
+        for wps in (1, 2):
+            for name, rd, dm in (("mfma", 0, 0), ("lds_reads", 8, 0), ("copies", 0, 4), ("reads_and_copies", 8, 4),
+                                 ("reads_and_half_copies", 8, 2)):
+                mix[f"{wps}_wave_per_simd_{name}"] = L.dllm_probe_mfma_mix(wps, rd, dm)
+        peaks["mfma_tflops_beside_lds_traffic"] = mix
         log(f"[bench] achievable: HBM read {hbm:.0f} GB/s, fp16 MFMA {mfma:.0f} TFLOP/s; streaming read at the "
-            f"projections' weight bytes: {peaks.get('read_gbs_at_weight_bytes')}")
+            f"projections' weight bytes: {peaks.get('read_gbs_at_weight_bytes')}; MFMA TFLOP/s beside LDS "
+            f"reads / copies: {', '.join(f'{k} {v:.0f}' for k, v in mix.items())}")
     b16 = None if (args.no_b16 or args.probe) else workload("llada8b_p128_g128")
     max_batch = max(w.batch, b16.batch if b16 else 0)
     max_seq = max(w.seq_len, b16.seq_len if b16 else 0)

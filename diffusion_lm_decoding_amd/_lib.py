@@ -21,6 +21,7 @@ RULE = {"threshold": 0, "factor": 1, "topk": 2, "budget": 3, "steps": 4}
 SYMBOLS = ("dllm_init_weights", "dllm_refresh_cache", "dllm_block_step", "dllm_block_step_noalloc",
            "dllm_staleness", "dllm_begin_decode",
            "dllm_decode", "dllm_set_timing", "dllm_get_timing", "dllm_probe_peaks", "dllm_probe_read",
+           "dllm_probe_mfma_mix",
            "dllm_set_device_limit",
            "dllm_destroy", "dllm_last_error")
 KERNEL_CLASSES = ("embed", "rmsnorm", "qkv", "attn", "oproj", "gateup", "down", "lmhead", "merge",
@@ -92,6 +93,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.dllm_probe_peaks.restype = C.c_int
     lib.dllm_probe_read.argtypes = [C.c_uint64, C.POINTER(C.c_double)]
     lib.dllm_probe_read.restype = C.c_int
+    lib.dllm_probe_mfma_mix.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_double)]
+    lib.dllm_probe_mfma_mix.restype = C.c_int
     lib.dllm_decode.argtypes = [P, C.POINTER(Canvas), C.POINTER(DecodeCfg), C.POINTER(Stats)]
     lib.dllm_decode.restype = C.c_int
     lib.dllm_set_timing.argtypes = [P, C.c_uint32, C.c_uint32]
@@ -161,6 +164,14 @@ def dllm_probe_peaks(nbytes: int = 8 << 30):
     hbm, mfma = C.c_double(0.0), C.c_double(0.0)
     check(load().dllm_probe_peaks(C.c_uint64(nbytes), C.byref(hbm), C.byref(mfma)))
     return hbm.value, mfma.value
+
+
+def dllm_probe_mfma_mix(waves_per_simd: int, lds_reads: int, dma_kib: int) -> float:
+    """MFMA TFLOP/s of device 0 with LDS reads / DMA copies beside the MFMA stream."""
+    t = C.c_double(0.0)
+    check(load().dllm_probe_mfma_mix(C.c_int32(waves_per_simd), C.c_int32(lds_reads), C.c_int32(dma_kib),
+                                     C.byref(t)))
+    return t.value
 
 
 def dllm_probe_read(nbytes: int) -> float:

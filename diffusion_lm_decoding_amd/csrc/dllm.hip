@@ -1155,6 +1155,64 @@ dllm_status dllm_probe_read(uint64_t bytes, double* gbs) {
   return done(DLLM_OK);
 }
 
+dllm_status dllm_probe_mfma_mix(int32_t waves_per_simd, int32_t lds_reads, int32_t dma_kib, double* tflops) {
+  g_err.clear();
+  if (!tflops || (waves_per_simd != 1 && waves_per_simd != 2) || (lds_reads != 0 && lds_reads != 8) ||
+      (dma_kib != 0 && dma_kib != 2 && dma_kib != 4))
+    return fail(DLLM_ERR_ARG, "waves_per_simd must be 1 or 2, lds_reads 0 or 8, dma_kib 0, 2 or 4, tflops non-NULL");
+  hipStream_t s = nullptr;
+  HIPCHK(hipStreamCreate(&s));
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  Frag16* src = nullptr;
+  float* sink = nullptr;
+  auto done = [&](dllm_status r) {
+    if (src) (void)hipFree(src);
+    if (sink) (void)hipFree(sink);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    (void)hipStreamDestroy(s);
+    return r;
+  };
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess)
+    return done(fail(DLLM_ERR_DEVICE, "hipEventCreate failed"));
+  if (hipMalloc(&src, 256 * 64 * sizeof(Frag16)) != hipSuccess || hipMalloc(&sink, 1024 * sizeof(float)) != hipSuccess) {
+    (void)hipGetLastError();
+    return done(fail(DLLM_ERR_OOM, "hipMalloc of the probe buffers failed"));
+  }
+  if (hipMemsetAsync(src, 0, 256 * 64 * sizeof(Frag16), s) != hipSuccess) return done(fail(DLLM_ERR_DEVICE, "hipMemsetAsync failed"));
+  const int nw = 4 * waves_per_simd, iters = 8000;
+  auto launch = [&](hipEvent_t a, hipEvent_t b) {
+    const dim3 g(256), blk(64 * nw);
+#define DLLM_MIX(NW, R, D) hipExtLaunchKernelGGL((mfma_mix_kernel<NW, R, D>), g, blk, 0, s, a, b, 0, src, iters, sink)
+    const int key = nw * 100 + lds_reads * 10 + dma_kib;
+    switch (key) {
+      case 400: DLLM_MIX(4, 0, 0); break;
+      case 480: DLLM_MIX(4, 8, 0); break;
+      case 402: DLLM_MIX(4, 0, 2); break;
+      case 404: DLLM_MIX(4, 0, 4); break;
+      case 482: DLLM_MIX(4, 8, 2); break;
+      case 484: DLLM_MIX(4, 8, 4); break;
+      case 800: DLLM_MIX(8, 0, 0); break;
+      case 880: DLLM_MIX(8, 8, 0); break;
+      case 802: DLLM_MIX(8, 0, 2); break;
+      case 804: DLLM_MIX(8, 0, 4); break;
+      case 882: DLLM_MIX(8, 8, 2); break;
+      default: DLLM_MIX(8, 8, 4); break;
+    }
+#undef DLLM_MIX
+  };
+  float best = 1e30f;
+  for (int rep = 0; rep < 4; ++rep) {
+    launch(e0, e1);
+    if (hipEventSynchronize(e1) != hipSuccess) return done(fail(DLLM_ERR_DEVICE, "probe kernel failed"));
+    float ms = 0.f;
+    (void)hipEventElapsedTime(&ms, e0, e1);
+    if (rep > 0 && ms < best) best = ms;   // the first launch warms up
+  }
+  *tflops = 256.0 * nw * iters * 16 * 32768.0 / (best * 1e-3) * 1e-12;
+  return done(DLLM_OK);
+}
+
 void dllm_destroy(dllm_ctx* ctx) {
   if (!ctx) return;
   (void)hipStreamSynchronize(ctx->stream);

@@ -545,6 +545,15 @@ __global__ __launch_bounds__(256) void rstd_kernel(const float* ssq, int tiles, 
   if (lane == 0) rstd[m] = 1.0f / sqrtf(s * inv_k + eps);
 }
 
+// f(integral_constant<int, i>) for i = B .. E-1, unrolled
+template <int B, int E, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 template <int V>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(V >= 0 && V < 64, "vmcnt range");
@@ -589,11 +598,14 @@ __global__ __launch_bounds__(64 * WN * WM) void gemm_big_kernel(GemmArgs a, Epi 
     src[q] = (isw ? a.W : a.X) + ((size_t)t * a.KT + (size_t)st_first * KS + kk) * 64 + lane;
     soff[q] = f;
   }
-  auto issue = [&](int st) {
-    const int buf = st % S;
+  // stage st's copies; stages past the end copy the last stage again (valid
+  // memory whose data is never used), so every iteration issues the same
+  // number of copies and every wait count below is a constant
+  auto issue = [&](int st, int buf) {
+    const size_t s = (size_t)min(st, nst - 1) * KS * 64;
 #pragma unroll
     for (int q = 0; q < LW; ++q)
-      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src[q] + (size_t)st * KS * 64),
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src[q] + s),
                                        (__attribute__((address_space(3))) void*)&lds[buf][soff[q]][0], 16, 0, 0);
   };
 
@@ -605,8 +617,7 @@ __global__ __launch_bounds__(64 * WN * WM) void gemm_big_kernel(GemmArgs a, Epi 
 
   // one (stage, k-fragment) step computes from one register set while the
   // next step's fragments are read from LDS into the other
-  auto read = [&](int st, int kk, Frag16 (&wf)[TN], Frag16 (&xf)[TM]) {
-    const int buf = st % S;
+  auto read = [&](int buf, int kk, Frag16 (&wf)[TN], Frag16 (&xf)[TM]) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) wf[j] = lds[buf][(wn * TN + j) * KS + kk][lane];
 #pragma unroll
@@ -618,59 +629,48 @@ __global__ __launch_bounds__(64 * WN * WM) void gemm_big_kernel(GemmArgs a, Epi 
 #pragma unroll
       for (int i = 0; i < TM; ++i) acc[j][i] = Mfma16<T>::mma(wf[j], xf[i], acc[j][i]);
   };
-  // this wave's copies of stage `st` have landed when at most `ahead` later
-  // stages are still outstanding (copies complete in issue order)
-  auto wait_stage = [&](int ahead) {
-    static_assert(S <= 8, "wait table");
-    switch (ahead) {
-      case 0: wait_vmcnt<0>(); break;
-      case 1: wait_vmcnt<(S > 1 ? 1 : 0) * LW>(); break;
-      case 2: wait_vmcnt<(S > 2 ? 2 : 0) * LW>(); break;
-      case 3: wait_vmcnt<(S > 3 ? 3 : 0) * LW>(); break;
-      case 4: wait_vmcnt<(S > 4 ? 4 : 0) * LW>(); break;
-      case 5: wait_vmcnt<(S > 5 ? 5 : 0) * LW>(); break;
-      default: wait_vmcnt<(S > 6 ? 6 : 0) * LW>(); break;
-    }
-  };
-  // all S buffers in flight; stage u + S is copied into buffer u % S once
-  // every wave has finished reading stage u
-#pragma unroll
-  for (int st = 0; st < S; ++st)
-    if (st < nst) issue(st);
-  wait_stage(min(nst, S) - 1);
+  // all S buffers in flight; stage st + S is copied into buffer st % S once
+  // every wave has finished reading stage st.  The loop body covers S stages
+  // so that every buffer index is a compile-time constant: with a run-time
+  // index the compiler cannot tell the LDS reads from the copies in flight
+  // and waits for all of them (vmcnt(0)) before each stage's first read.
+  static_for<0, S>([&](auto s_c) { issue(decltype(s_c)::value, decltype(s_c)::value); });
+  wait_vmcnt<(S - 1) * LW>();
   __builtin_amdgcn_s_barrier();
-  // two register sets; step t = st*KS + kk computes from set t%2 (a compile-
-  // time index: stages are unrolled in pairs) while set (t+1)%2 is loaded.
-  // The loads are unconditional (the last step re-reads its own fragments)
-  // so no branch joins sit between them and the MFMAs.
+  // two register sets; step t = st*KS + kk computes from set t%2 (S*KS is
+  // even for every configuration, so a loop body starts on set 0)
   static_assert(KS == 1 || KS == 2, "k-fragments per stage");
+  static_assert((S * KS) % 2 == 0, "register sets alternate across the loop body");
   Frag16 fw[2][TN], fx[2][TM];
   read(0, 0, fw[0], fx[0]);
-  const int nsteps = nst * KS;
-  auto do_step = [&](int st, int kk, auto cur_c) {
-    constexpr int cur = decltype(cur_c)::value, nxt = 1 - cur;
-    const bool last = st * KS + kk + 1 == nsteps;
-    if (kk + 1 < KS) {
-      read(st, kk + 1, fw[nxt], fx[nxt]);
-    } else {
-      // next stage: its copies landed everywhere, stage st is read everywhere
-      wait_stage(last ? 0 : min(nst, st + S) - st - 2);
-      wait_lgkmcnt0();
-      __builtin_amdgcn_s_barrier();
-      if (st + S < nst) issue(st + S);
-      read(last ? st : st + 1, 0, fw[nxt], fx[nxt]);
-    }
-    mma(fw[cur], fx[cur]);
+  auto stage = [&](int st, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    static_for<0, KS>([&](auto kk_c) {
+      constexpr int kk = decltype(kk_c)::value;
+      constexpr int cur = (buf * KS + kk) % 2, nxt = 1 - cur;
+      if constexpr (kk + 1 < KS) {
+        read(buf, kk + 1, fw[nxt], fx[nxt]);
+      } else {
+        // stage st + 1 landed (S - 2 later stages in flight) and every wave
+        // has read stage st: its buffer takes stage st + S
+        wait_vmcnt<(S - 2) * LW>();
+        wait_lgkmcnt0();
+        __builtin_amdgcn_s_barrier();
+        issue(st + S, buf);
+        read((buf + 1) % S, 0, fw[nxt], fx[nxt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mma(fw[cur], fx[cur]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
-  auto do_stage = [&](int st, auto base_c) {
-    constexpr int b0 = decltype(base_c)::value;
-    do_step(st, 0, std::integral_constant<int, b0>{});
-    if constexpr (KS == 2) do_step(st, 1, std::integral_constant<int, 1 - b0>{});
-  };
-  for (int st = 0; st < nst; st += 2) {
-    do_stage(st, std::integral_constant<int, 0>{});
-    if (st + 1 < nst) do_stage(st + 1, std::integral_constant<int, (KS & 1)>{});
-  }
+  int st = 0;
+  for (; st + S <= nst; st += S)
+    static_for<0, S>([&](auto i_c) { stage(st + decltype(i_c)::value, i_c); });
+  static_for<0, S>([&](auto i_c) {
+    if (st + decltype(i_c)::value < nst) stage(st + decltype(i_c)::value, i_c);
+  });
+  wait_vmcnt<0>();   // the copies past the end
   if (k_splits > 1) {
     // raw partial tiles; the reduce kernel scales by 1/rms and runs the epilogue
 #pragma unroll

@@ -3,8 +3,10 @@
 //  * hbm_read_kernel: every 16-byte word of a buffer much larger than the
 //    memory-side cache read once, in contiguous 32 KiB chunks per workgroup;
 //  * mfma_loop_kernel: each wave keeps 4 independent 32x32x16 fp16 MFMA
-//    accumulator chains busy from registers (no memory traffic).
-// Both write a value derived from what they computed, so nothing is elided.
+//    accumulator chains busy from registers (no memory traffic);
+//  * mfma_mix_kernel: the same MFMA stream with LDS reads and DMA copies into
+//    LDS issued beside it, in the proportions of a large-M GEMM's main loop.
+// All write a value derived from what they computed, so nothing is elided.
 #pragma once
 #include "mfma.h"
 
@@ -47,6 +49,62 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* sink) 
 #pragma unroll
   for (int c = 0; c < 4; ++c) s += acc[c][0] + acc[c][5] + acc[c][10] + acc[c][15];
   if (s == 1234.5f) sink[0] = s;
+}
+
+// One workgroup of NW waves per CU.  Per iteration each wave issues DMA
+// global_load_lds_dwordx4 copies (1 KiB each, from a buffer that stays in L2,
+// into LDS blocks nobody reads), READS ds_read_b128 (1 KiB each, into one of
+// two register sets) and 16 32x32x16 fp16 MFMAs on 4 accumulators that use
+// the other register set, so the MFMAs never wait on this iteration's reads;
+// copies older than two iterations are waited for.
+template <int NW, int READS, int DMA>
+__global__ __launch_bounds__(64 * NW) void mfma_mix_kernel(const Frag16* src, int iters, float* sink) {
+  static_assert(READS <= 8 && DMA <= 8, "per-iteration budget");
+  __shared__ Frag16 rd_buf[32][64];                        // read by ds_read_b128
+  __shared__ Frag16 cp_buf[DMA > 0 ? 8 * NW : 1][64];      // written by the copies
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 32 * 64; i += 64 * NW) rd_buf[i / 64][i % 64] = Frag16{(uint32_t)i, 1u, 2u, 3u};
+  __syncthreads();
+  Frag16 ra[8], rb[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ra[j] = rb[j] = Frag16{(uint32_t)(lane * 0x3c00u), 0x3c003c00u, (uint32_t)j, 0u};
+  f32x16 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+  auto step = [&](int it, Frag16 (&rd)[8], const Frag16 (&mf)[8]) {
+    if constexpr (DMA > 0) {
+#pragma unroll
+      for (int q = 0; q < DMA; ++q)
+        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + (size_t)((it * DMA + q) & 255) * 64 + lane),
+                                         (__attribute__((address_space(3))) void*)&cp_buf[wave * 8 + q][0], 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < READS; ++j) rd[j] = rd_buf[(it * 8 + j + wave) & 31][lane];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      f16x8 x, y;
+      __builtin_memcpy(&x, &mf[m & 7], 16);
+      __builtin_memcpy(&y, &mf[(m + 3) & 7], 16);
+      acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(x, y, acc[m & 3], 0, 0, 0);
+    }
+    if constexpr (DMA > 0) {
+      constexpr int V = 2 * DMA;   // gfx9 vmcnt encoding: [3:0] | [15:14] << 4
+      __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | (15 << 8) | ((V >> 4) << 14));
+    }
+  };
+  for (int it = 0; it + 1 < iters; it += 2) {
+    step(it, ra, rb);
+    step(it + 1, rb, ra);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += (float)(ra[j].x ^ rb[j].y);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) s += acc[c][lane & 15];
+  if (s == 1234.5f) sink[threadIdx.x] = s;
 }
 
 }  // namespace dllm

@@ -374,6 +374,20 @@ dllm_status dllm_probe_peaks(uint64_t bytes, double* hbm_gbs, double* mfma_f16_t
  * Errors: DLLM_ERR_ARG (bytes < 1 MiB or gbs NULL), DLLM_ERR_OOM, DLLM_ERR_DEVICE. */
 dllm_status dllm_probe_read(uint64_t bytes, double* gbs);
 
+/* Matrix-pipe throughput of an MFMA stream that shares the CU with LDS
+ * traffic: one workgroup of 4 * waves_per_simd waves per CU, each wave issuing
+ * per 16 fp16 32x32x16 MFMAs (4 accumulators, operands in registers and
+ * independent of the loads) `lds_reads` 1 KiB ds_read_b128 reads and
+ * `dma_kib` 1 KiB global_load_lds copies (from a buffer that stays in L2,
+ * into LDS).  These are the proportions of a large-M projection's main loop
+ * (a 128x128 wave tile reads 8 KiB of operands per 16 MFMAs; a 256x256
+ * workgroup tile copies 4 KiB per wave per 16 MFMAs).  *tflops = MFMA
+ * TFLOP/s of the whole device, best of 3 launches.  Allocates 260 KiB for the
+ * duration of the call.
+ * Errors: DLLM_ERR_ARG (waves_per_simd not 1 or 2, lds_reads not 0 or 8,
+ *   dma_kib not 0, 2 or 4, tflops NULL), DLLM_ERR_OOM, DLLM_ERR_DEVICE. */
+dllm_status dllm_probe_mfma_mix(int32_t waves_per_simd, int32_t lds_reads, int32_t dma_kib, double* tflops);
+
 /* Process-wide cap on the device memory a context may hold: dllm_init_weights
  * fails with DLLM_ERR_OOM, before allocating past it, when the packed weights,
  * KV cache and workspaces of the requested shape exceed `bytes`, and
