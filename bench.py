@@ -235,6 +235,8 @@ def main():
         out["b16_projection_mfma_fraction"] = b16_projections(eng, b16, L)
     eng.close()
     del eng
+    if b16 is not None and shape.name == "llada8b":
+        out["b16_projection_mfma_fraction"]["library_yardstick"] = library_yardstick(shape)
     if not args.no_cpu_baseline:
         sample = cpu_baseline(shape, host_weights, w, prompt, target, alpha, args.cpu_steps)
         out["cpu_baseline"] = cpu_baseline_record(sample, w, steps / args.steps, committed / args.steps,
@@ -264,6 +266,39 @@ def probe(eng, w, prompt, target, alpha, n_steps, dev):
     print(json.dumps({"probe": w.name, "denoising_steps": n_steps, "copy_bytes_read": n * 4,
                       "copy_bytes_written": n * 4}), flush=True)
     eng.close()
+
+
+def library_yardstick(shape, reps=10):
+    """Context for the large-M projections: the vendor library's fp16 GEMM
+    (torch.nn.functional.linear -> hipBLASLt, weights [out, in] as a
+    projection stores them, fp32 accumulation, plain output, no fused
+    epilogue) at the projections' shapes with 512 rows (batch-16 step) and 768
+    rows (cache refresh), TFLOP/s from the best of `reps` timed calls with cold
+    weights (two weight copies alternate)."""
+    import torch
+    import torch.nn.functional as F
+    d, f = shape.d_model, shape.d_ffn
+    out = {}
+    for m in (512, 768):
+        for name, n, k in (("qkv", 3 * d, d), ("oproj", d, d), ("gateup", 2 * f, d), ("down", d, f)):
+            x = torch.randn(m, k, dtype=torch.float16, device="cuda")
+            ws = [torch.randn(n, k, dtype=torch.float16, device="cuda") * 0.02 for _ in range(2)]
+            F.linear(x, ws[0])
+            torch.cuda.synchronize()
+            best = 1e30
+            for i in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                F.linear(x, ws[i % 2])
+                e1.record()
+                e1.synchronize()
+                best = min(best, e0.elapsed_time(e1))
+            out[f"{name}_m{m}"] = {"us": best * 1e3, "tflops": 2.0 * m * n * k / (best * 1e-3) / 1e12}
+            del x, ws
+    torch.cuda.empty_cache()
+    log("[bench] library fp16 GEMM yardstick: " + ", ".join(f"{k} {v['us']:.0f} us ({v['tflops']:.0f} TF)"
+                                                             for k, v in out.items()))
+    return out
 
 
 def b16_projections(eng, w, L, n_steps=3):
