@@ -386,8 +386,11 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(AttnArgs a) {
   const T* kc = static_cast<const T*>(a.kc) + ((size_t)b * a.H + h) * a.seq_pad * DH;
   const T* vt = static_cast<const T*>(a.vt) + ((size_t)b * a.H + h) * DH * a.seq_pad;
 
-  auto issue = [&](int t) {
-    const int kb = t * 32, st = t % S;
+  // tile t's copies into ring slot `slot`; tiles past the workgroup's last
+  // copy that tile again (valid memory, never used), so every loop body
+  // issues the same copies and every wait below is a constant
+  auto issue = [&](int t, int slot) __attribute__((always_inline)) {
+    const int kb = min(t, nt - 1) * 32;
 #pragma unroll
     for (int q = 0; q < LW; ++q) {
       const int f = wave + q * NW;
@@ -399,24 +402,10 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(AttnArgs a) {
         src = vt + (size_t)(i * 32 + (lane & 31)) * a.seq_pad + kb + (2 * c + hf) * 8;
       }
       __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)&ring[st][f][0], 16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)&ring[slot][f][0], 16, 0, 0);
     }
   };
-  auto wait_tile = [&](int ahead) {   // this wave's copies of a tile landed, `ahead` later tiles outstanding
-    switch (ahead) {
-      case 0: wait_vmcnt<0>(); break;
-      case 1: wait_vmcnt<(S > 1 ? 1 : 0) * LW>(); break;
-      case 2: wait_vmcnt<(S > 2 ? 2 : 0) * LW>(); break;
-      case 3: wait_vmcnt<(S > 3 ? 3 : 0) * LW>(); break;
-      case 4: wait_vmcnt<(S > 4 ? 4 : 0) * LW>(); break;
-      case 5: wait_vmcnt<(S > 5 ? 5 : 0) * LW>(); break;
-      default: wait_vmcnt<(S > 6 ? 6 : 0) * LW>(); break;
-    }
-  };
-#pragma unroll
-  for (int t = 0; t < S; ++t)
-    if (t < nt) issue(t);
-
+  // the queries first: the wait for a tile's copies then covers them too
   Frag16 qf[NQF];
   const T* qrow = static_cast<const T*>(a.q) + (size_t)m * a.d + h * DH + 8 * hf;
 #pragma unroll
@@ -427,24 +416,67 @@ __global__ __launch_bounds__(64 * NW) void attn_wide_kernel(AttnArgs a) {
   for (int i = 0; i < ND; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
-
-  for (int t = 0; t < nt; ++t) {
-    wait_tile(min(nt, t + S) - t - 1);
-    __builtin_amdgcn_s_barrier();
-    const int st = t % S;
-    Frag16 kf[NQF], vf[ND][2];
+  static_assert(S % 2 == 0 && S >= 2, "ring of an even number of tiles");
+  auto read = [&](int slot, Frag16 (&k)[NQF], Frag16 (&v)[ND][2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < NQF; ++c) kf[c] = ring[st][c][lane];
+    for (int c = 0; c < NQF; ++c) k[c] = ring[slot][c][lane];
 #pragma unroll
     for (int i = 0; i < ND; ++i)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) vf[i][c] = ring[st][NQF + 2 * i + c][lane];
-    attn_tile16<T, DH>(qf, kf, vf, t * 32, limit, a.scale_log2, mrun, lrun, o, lane);
-    // stage st is read by every wave before it is refilled with tile t + S
-    wait_lgkmcnt0();
+      for (int c = 0; c < 2; ++c) v[i][c] = ring[slot][NQF + 2 * i + c][lane];
+  };
+  // Ring slots are compile-time constants (S tiles per loop body): with a
+  // run-time slot index the compiler waits for every copy in flight before
+  // each LDS read.  One barrier per tile.
+  // DB (4 waves, whose registers hold two tiles): tile t computes from one
+  // register set while tile t + 1 is read into the other; S tiles in flight.
+  // Otherwise one register set: a tile is read after the barrier that makes
+  // it visible; S - 1 tiles in flight.
+  constexpr bool DB = NW == 4;
+  int t = 0;
+  if constexpr (DB) {
+    static_for<0, S>([&](auto t_c) { issue(decltype(t_c)::value, decltype(t_c)::value); });
+    Frag16 kf[2][NQF], vf[2][ND][2];
+    wait_vmcnt<(S - 1) * LW>();   // the queries and tile 0 have landed
     __builtin_amdgcn_s_barrier();
-    if (t + S < nt) issue(t + S);
+    read(0, kf[0], vf[0]);
+    auto tile = [&](int tt, auto slot_c) __attribute__((always_inline)) {
+      constexpr int slot = decltype(slot_c)::value, cur = slot % 2, nxt = 1 - cur;
+      // tile tt + 1 landed (S - 2 later tiles in flight) and every wave has
+      // read tile tt into registers: its slot takes tile tt + S
+      wait_vmcnt<(S - 2) * LW>();
+      wait_lgkmcnt0();
+      __builtin_amdgcn_s_barrier();
+      issue(tt + S, slot);
+      read((slot + 1) % S, kf[nxt], vf[nxt]);
+      attn_tile16<T, DH>(qf, kf[cur], vf[cur], tt * 32, limit, a.scale_log2, mrun, lrun, o, lane);
+    };
+    for (; t + S <= nt; t += S)
+      static_for<0, S>([&](auto i_c) __attribute__((always_inline)) { tile(t + decltype(i_c)::value, i_c); });
+    static_for<0, S>([&](auto i_c) __attribute__((always_inline)) {
+      if (t + decltype(i_c)::value < nt) tile(t + decltype(i_c)::value, i_c);
+    });
+  } else {
+    static_for<0, S - 1>([&](auto t_c) { issue(decltype(t_c)::value, decltype(t_c)::value); });
+    Frag16 kf[NQF], vf[ND][2];
+    auto tile = [&](int tt, auto slot_c) __attribute__((always_inline)) {
+      constexpr int slot = decltype(slot_c)::value;
+      // tile tt landed (S - 2 later tiles in flight) and every wave has read
+      // tile tt - 1: its slot takes tile tt + S - 1
+      wait_vmcnt<(S - 2) * LW>();
+      wait_lgkmcnt0();
+      __builtin_amdgcn_s_barrier();
+      issue(tt + S - 1, (slot + S - 1) % S);
+      read(slot, kf, vf);
+      attn_tile16<T, DH>(qf, kf, vf, tt * 32, limit, a.scale_log2, mrun, lrun, o, lane);
+    };
+    for (; t + S <= nt; t += S)
+      static_for<0, S>([&](auto i_c) __attribute__((always_inline)) { tile(t + decltype(i_c)::value, i_c); });
+    static_for<0, S>([&](auto i_c) __attribute__((always_inline)) {
+      if (t + decltype(i_c)::value < nt) tile(t + decltype(i_c)::value, i_c);
+    });
   }
+  wait_vmcnt<0>();   // the copies past the end
   if (!valid) return;
   const float inv = 1.0f / lrun;
   T* out = static_cast<T*>(a.out);
