@@ -414,9 +414,10 @@ constexpr int kNumBigCfgs = sizeof(kBigCfgs) / sizeof(kBigCfgs[0]);
 // idle (few output tiles, long K: the down and O projections at 128-512
 // rows), the K range is split over 2-4 workgroups per tile whose fp32 partial
 // tiles are added, in split order, by gemm_split_reduce_kernel, which also
-// runs the epilogue.  The split costs the partial tiles' round trip and the
-// second launch: about 4.6 us per million outputs, at least 3 us (same
-// sweeps).
+// runs the epilogue.  The split costs the second launch and the partial
+// tiles' round trip: about 2.5 us plus 0.14 us per MB of partials read and
+// epilogue traffic (4 bytes per output and split, about 10 more per output
+// for the residual update), measured on MI355X at 0.5-8M outputs.
 constexpr int kMaxKSplits = 4;
 constexpr int kMinStagesPerSplit = 16;
 // The Q/K/V epilogue (rotary, scattered cache writes) costs the reduce kernel
@@ -438,7 +439,7 @@ dllm_status launch_big(dllm_ctx* c, GemmArgs a, const Epi& epi) {
                      (size_t)sp * a.m_tiles * a.n_tiles * 256 > c->gemm_part_floats))
         break;
       const double t = std::ceil(nwg * sp / 256.0) * (g.f0_us + g.step_ns * 1e-3 * ((double)a.KT / sp)) +
-                       (sp > 1 ? std::max(3.0, 4.6e-6 * outputs - 5.3) : 0.0);
+                       (sp > 1 ? 2.5 + 0.14e-6 * outputs * (4.0 * sp + 10.0) : 0.0);
       if (t < best_t) { best_t = t; best = i; best_s = sp; }
     }
   }
@@ -459,9 +460,13 @@ dllm_status launch_big(dllm_ctx* c, GemmArgs a, const Epi& epi) {
     case 7: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 6, 8, 2, 2, 2, 5>), grid(6, 8), dim3(256), 0, c->stream, a, epi); break;
     default: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 8, 2, 2, 1, 6>), grid(8, 8), dim3(256), 0, c->stream, a, epi); break;
   }
-  if (best_s > 1)
-    hipLaunchKernelGGL(gemm_split_reduce_kernel<Epi>, dim3((unsigned)cdiv(a.m_tiles * a.n_tiles, 4)), dim3(256), 0,
-                       c->stream, a, epi);
+  if (best_s > 1) {
+    const dim3 rg((unsigned)cdiv(a.m_tiles * a.n_tiles, 4));
+    static_assert(kMaxKSplits == 4, "one reduce instantiation per split count");
+    if (best_s == 2) hipLaunchKernelGGL((gemm_split_reduce_kernel<2, Epi>), rg, dim3(256), 0, c->stream, a, epi);
+    else if (best_s == 3) hipLaunchKernelGGL((gemm_split_reduce_kernel<3, Epi>), rg, dim3(256), 0, c->stream, a, epi);
+    else hipLaunchKernelGGL((gemm_split_reduce_kernel<4, Epi>), rg, dim3(256), 0, c->stream, a, epi);
+  }
   return DLLM_OK;
 }
 
@@ -607,7 +612,14 @@ dllm_status launch_attn(dllm_ctx* c, int layer, const Fwd& f) {
     }
   }
   hipLaunchKernelGGL((attn_kernel<T, DH, 4>), dim3(nwg, splits), dim3(256), 0, c->stream, a);
-  if (splits > 1) hipLaunchKernelGGL((attn_merge_kernel<T, DH>), dim3(nwg, DH / 32), dim3(256), 0, c->stream, a, nwg);
+  if (splits > 1) {
+    static_assert(kMaxAttnSplits == 16, "one merge instantiation per power-of-two share bound");
+    const dim3 mg(nwg, DH / 32);
+    if (splits <= 2) hipLaunchKernelGGL((attn_merge_kernel<T, DH, 2>), mg, dim3(256), 0, c->stream, a, nwg);
+    else if (splits <= 4) hipLaunchKernelGGL((attn_merge_kernel<T, DH, 4>), mg, dim3(256), 0, c->stream, a, nwg);
+    else if (splits <= 8) hipLaunchKernelGGL((attn_merge_kernel<T, DH, 8>), mg, dim3(256), 0, c->stream, a, nwg);
+    else hipLaunchKernelGGL((attn_merge_kernel<T, DH, 16>), mg, dim3(256), 0, c->stream, a, nwg);
+  }
   return tm.done();
 }
 

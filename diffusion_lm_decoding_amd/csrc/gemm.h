@@ -306,6 +306,14 @@ struct GemmArgs {
   const int* m_count;
 };
 
+// Pipelined skinny loop over a rotated K order (see gemm_skinny_kernel): on
+// for the Q/K/V projection, whose 32-row LLaDA-8B launch measured 20.5 ->
+// 19.7 us with it on MI355X (the same as with its activation loads removed);
+// O and down measured no gain.  Rotation changes the order in which each
+// wave accumulates its K range, not the result's reproducibility.
+template <class Epi> constexpr bool kRotateK = false;
+template <typename T> constexpr bool kRotateK<EpiQKV<T>> = true;
+
 // Workgroup i runs on XCD i % 8; map consecutive logical ids to one XCD so the
 // workgroups that share weight tiles share an L2.
 __device__ __forceinline__ int xcd_remap(int hw, int total) {
@@ -379,15 +387,21 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(GemmArgs a, Epi ep
   const int nbat = (k1 - k0) / U;
   int kt = k0;
   if constexpr (PIPE) {
-    if (nbat > 0) load(wa, xa, kt);
+    // batch b of the wave's K range is batch (b + rot) % nbat: with kRotateK
+    // every workgroup starts at a different point of the range
+    const int rot = kRotateK<Epi> && nbat > 1 ? lin % nbat : 0;
+    auto kb = [&](int b) {
+      const int bb = b + rot;
+      return k0 + (bb >= nbat ? bb - nbat : bb) * U;
+    };
+    if (nbat > 0) load(wa, xa, kb(0));
     for (int b = 0; b < nbat; b += 2) {
-      if (b + 1 < nbat) load(wb, xb, kt + U);
+      if (b + 1 < nbat) load(wb, xb, kb(b + 1));
       compute(wa, xa);
       if (b + 1 < nbat) {
-        if (b + 2 < nbat) load(wa, xa, kt + 2 * U);
+        if (b + 2 < nbat) load(wa, xa, kb(b + 2));
         compute(wb, xb);
       }
-      kt += 2 * U;
     }
   } else {
     // one register set (fewer VGPRs, several workgroups resident per CU); the
@@ -708,10 +722,13 @@ __global__ __launch_bounds__(64 * WN * WM) void gemm_big_kernel(GemmArgs a, Epi 
 }
 
 // Second half of a K-split gemm_big_kernel launch: one wave per 16x16 output
-// tile adds the k_splits partial tiles in split order (so results are
-// run-to-run identical), applies the row's 1/rms and runs the epilogue
-// exactly once.  Grid: ceil(m_tiles * n_tiles / 4) workgroups of 4 waves.
-template <class Epi>
+// tile adds the KS partial tiles in split order (so results are run-to-run
+// identical), applies the row's 1/rms and runs the epilogue exactly once.
+// KS is a compile-time constant, so all KS partial loads are issued before the
+// first is used (with a run-time count the reduce took 1.5-1.6x as long on
+// MI355X: 9.3 -> 6.0 us for two splits of 2M outputs, 15.7 -> 9.7 us for
+// four).  Grid: ceil(m_tiles * n_tiles / 4) workgroups of 4 waves.
+template <int KS, class Epi>
 __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs a, Epi epi) {
   const int lane = threadIdx.x & 63;
   const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -719,14 +736,12 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs a, Epi 
   const int mt = tile / a.n_tiles, nt = tile % a.n_tiles;
   const size_t stride = (size_t)a.m_tiles * a.n_tiles * 256;
   const float* p = a.part + ((size_t)tile * 64 + lane) * 4;
-  f32x4 parts[8];
+  f32x4 parts[KS];
 #pragma unroll
-  for (int s = 0; s < 8; ++s)
-    if (s < a.k_splits) parts[s] = *reinterpret_cast<const f32x4*>(p + s * stride);
+  for (int s = 0; s < KS; ++s) parts[s] = *reinterpret_cast<const f32x4*>(p + s * stride);
   f32x4 v = parts[0];
 #pragma unroll
-  for (int s = 1; s < 8; ++s)
-    if (s < a.k_splits) v += parts[s];
+  for (int s = 1; s < KS; ++s) v += parts[s];
   if (a.ssq) v *= a.rstd[min(mt * 16 + (lane & 15), a.ssq_ld - 1)];
   epi(nt, mt, v, lane);
 }
