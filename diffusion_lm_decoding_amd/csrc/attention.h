@@ -313,7 +313,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
 // its ND 32-dim output tiles only, so it writes final outputs and no merge
 // kernel follows.  Its NW waves take the key tiles round-robin, requesting
 // the next tile's fragments before the current tile's math, and are merged
-// by the LDS tree.
+// by the LDS tree.  With ND = DH / 32 (one slice: the whole head) it also
+// serves a full round of blocks that needs no key shares (batch >= 8 steps).
 template <typename T, int DH, int NW, int ND>
 __global__ __launch_bounds__(64 * NW) void attn_dslice_kernel(AttnArgs a) {
   static_assert(sizeof(T) == 2, "16-bit caches");

@@ -169,6 +169,14 @@ struct EpiResidual {
   }
 };
 
+// SiLU g / (1 + e^-g) from the hardware's 2^x and reciprocal (each within a
+// few ulp of fp32; the product is rounded to 16 bits after): about 2 us less
+// per large-M gate/up launch on MI355X than an IEEE division of expf.  Very
+// negative g: 2^x overflows to inf, its reciprocal is 0, silu -> -0.
+__device__ __forceinline__ float silu(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
+}
+
 // SwiGLU: packed rows 2i / 2i+1 are gate row i / up row i, so each lane holds
 // (g_i, u_i, g_{i+1}, u_{i+1}); a_i = silu(g_i) * u_i goes to the packed input
 // of the down projection.
@@ -184,8 +192,7 @@ struct EpiSwiGLU {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const float gt = acc[2 * t], up = acc[2 * t + 1];
-      const float s = gt / (1.0f + expf(-gt));
-      h[t] = s * up;
+      h[t] = silu(gt) * up;
     }
     if constexpr (sizeof(T) == 2) {
       store_run<T, 2>(a + packed_off<T>(m, i0, F), h);  // i0 even: adjacent slots
