@@ -158,6 +158,10 @@ struct dllm_ctx {
   float* attn_ws = nullptr;
   size_t attn_ws_floats = 0;
   int head_group = 1;         // vocabulary tiles per LM-head partial of the last head launch
+  // set by dllm_decode around each step: an upper bound on the block rows
+  // still masked (block rows minus the commits read back since the block
+  // began), or -1 when unknown (dllm_block_step called directly)
+  int head_rows_hint = -1;
 
   // one device status block [ncommit(max_batch) | done(max_batch) | err(4)],
   // mirrored into h_pin (same layout) by the select/commit kernel
@@ -751,7 +755,11 @@ dllm_status eval_block(dllm_ctx* c, const dllm_canvas* cv, const dllm_decode_cfg
   EpiLMHead eh{HR, B, d->gen_len, s - d->prompt_len, cv->bias_target, cv->bias_alpha, m.mask_id, m.vocab,
                c->n_vtiles, ws.pmax, ws.psum, ws.parg, dbg_logits, rowmap, count};
   c->head_group = 1;   // the skinny launch sets its n-tiles per workgroup
-  TRY(launch_gemm<T>(c, DLLM_K_LMHEAD, compact ? c->xc : c->xh, c->wlm, HR, m.vocab, m.d_model, eh,
+  // compacted rows: launched for the host's bound on the masked rows when it
+  // has one, so the kernel and tile shape follow the rows that need logits
+  // (the device count, never above the bound, still limits the work)
+  const int m_head = (compact && c->head_rows_hint >= 0) ? std::min(HR, std::max(1, c->head_rows_hint)) : HR;
+  TRY(launch_gemm<T>(c, DLLM_K_LMHEAD, compact ? c->xc : c->xh, c->wlm, m_head, m.vocab, m.d_model, eh,
                      compact ? c->ssq_c : c->ssq_head, HR, count));
   if (after_head) HIPCHK(hipEventRecord(after_head, c->stream));
   const int n_parts = c->n_vtiles / c->head_group;
@@ -1423,7 +1431,7 @@ dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cf
   double ms_refresh = 0.0, ms_step = 0.0, ms_select = 0.0;
   int64_t split_steps = 0;
   int64_t steps = 0, refreshes = 0, committed = 0;
-  std::vector<int> nc(cfg->batch), done(cfg->batch), was_done(cfg->batch);
+  std::vector<int> nc(cfg->batch), done(cfg->batch), was_done(cfg->batch), masked(cfg->batch);
   std::vector<int64_t> seq_steps(cfg->batch, 0);
   const bool steps_rule = cfg->rule == DLLM_RULE_STEPS;
   const int max_in_block = steps_rule ? cfg->k : cfg->block_len;
@@ -1452,14 +1460,21 @@ dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cf
     if (cached) st = timed_refresh(0, j, 0);
     int in_block = 0;
     std::fill(was_done.begin(), was_done.end(), 0);
+    // at most block_len rows of each sequence are masked when a block begins
+    std::fill(masked.begin(), masked.end(), cfg->block_len);
     while (st == DLLM_OK) {
       if (cached && cfg->refresh_every > 0 && in_block > 0 && in_block % cfg->refresh_every == 0) {
         st = timed_refresh(0, j, in_block);
         if (st != DLLM_OK) break;
       }
       hipEvent_t* step_ev = (stats && steps % kSplitEvery == 0) ? ev.e + 2 : nullptr;
+      int bound = 0;
+      for (int b = 0; b < cfg->batch; ++b) bound += masked[b];
+      ctx->head_rows_hint = bound;
       st = block_step(ctx, canvas, cfg, j, nc.data(), done.data(), nullptr, nullptr, nullptr, step_ev);
+      ctx->head_rows_hint = -1;
       if (st != DLLM_OK) break;
+      for (int b = 0; b < cfg->batch; ++b) masked[b] = done[b] ? 0 : std::max(0, masked[b] - nc[b]);
       double ms_fwd = -1.0, ms_sel = -1.0;
       if (step_ev) {   // the step returned after its status readback: the events are complete
         ms_fwd = ev.ms(2, 3, &st);
