@@ -408,7 +408,10 @@ dllm_status launch_skinny_nt(dllm_ctx* c, const Timed& tm, const GemmArgs& a, co
 // four at 2048; 192 x 128 does the same for the Q/K/V projection at 512 rows
 // (92 -> 73 us); 128 x 64 serves short O and down projections at 128-512 rows;
 // 96 x 128 fills one round for Q/K/V at 256 rows (56 -> 47 us) and gate/up at
-// 128 (46 -> 40 us).
+// 128 (46 -> 40 us).  The 192 x 256 tile runs one k-fragment per stage in a
+// 4-deep ring with its copies spread over the MFMAs (gate/up at 512 rows
+// 94-98 -> 88 us, down at 768 rows split 3 ways 90 -> 82 us against two
+// k-fragments per stage in 2 stages; its cost entry predates that).
 struct BigCfg { int ntw, mtw; double f0_us, step_ns; };
 constexpr BigCfg kBigCfgs[] = {{12, 12, 14.5, 521.0}, {16, 8, 11.5, 506.0}, {8, 8, 2.3, 357.0}, {8, 6, 2.4, 280.0},
                                {12, 16, 25.5, 562.0}, {12, 8, 7.2, 423.0}, {8, 4, 2.0, 236.0}, {6, 8, 2.0, 310.0}};
@@ -447,7 +450,7 @@ dllm_status launch_big(dllm_ctx* c, GemmArgs a, const Epi& epi) {
       if (t < best_t) { best_t = t; best = i; best_s = sp; }
     }
   }
-  // every configuration but the fallback takes two k-fragments per stage
+  // most configurations take two k-fragments per stage (K a multiple of 64)
   if (a.KT % 2 != 0) { best = -1; best_s = 1; }
   a.k_splits = best_s;
   a.part = c->gemm_part;
@@ -458,7 +461,7 @@ dllm_status launch_big(dllm_ctx* c, GemmArgs a, const Epi& epi) {
     case 1: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 16, 8, 4, 2, 2, 3>), grid(16, 8), dim3(512), 0, c->stream, a, epi); break;
     case 2: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 8, 2, 2, 2, 4>), grid(8, 8), dim3(256), 0, c->stream, a, epi); break;
     case 3: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 6, 2, 2, 2, 5>), grid(8, 6), dim3(256), 0, c->stream, a, epi); break;
-    case 4: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 12, 16, 2, 4, 2, 2>), grid(12, 16), dim3(512), 0, c->stream, a, epi); break;
+    case 4: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 12, 16, 2, 4, 1, 4>), grid(12, 16), dim3(512), 0, c->stream, a, epi); break;
     case 5: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 12, 8, 4, 2, 2, 3>), grid(12, 8), dim3(512), 0, c->stream, a, epi); break;
     case 6: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 8, 4, 2, 2, 2, 6>), grid(8, 4), dim3(256), 0, c->stream, a, epi); break;
     case 7: hipLaunchKernelGGL((gemm_big_kernel<T, Epi, 6, 8, 2, 2, 2, 5>), grid(6, 8), dim3(256), 0, c->stream, a, epi); break;

@@ -587,8 +587,10 @@ template <typename T, class Epi, int NTW, int MTW, int WN, int WM, int KS, int S
 __global__ __launch_bounds__(64 * WN * WM) void gemm_big_kernel(GemmArgs a, Epi epi) {
   constexpr int NWAVE = WN * WM;
   constexpr int F = KS * (NTW + MTW);     // fragments per stage
-  constexpr int LW = F / NWAVE;           // copies per wave per stage
-  static_assert(F % NWAVE == 0, "stage fragments must split evenly over the waves");
+  // copies per wave per stage; when F is not a multiple of the waves, the
+  // spare copy slots repeat the stage's last fragment (the same bytes into
+  // the same LDS block), so every wave issues LW copies and waits alike
+  constexpr int LW = (F + NWAVE - 1) / NWAVE;
   constexpr int TN = NTW / WN, TM = MTW / WM;  // wave tile in 16x16 tiles
   static_assert(NTW % WN == 0 && MTW % WM == 0, "wave grid must divide the tile");
   __shared__ Frag16 lds[S][F][64];
@@ -611,7 +613,7 @@ __global__ __launch_bounds__(64 * WN * WM) void gemm_big_kernel(GemmArgs a, Epi 
   int soff[LW];
 #pragma unroll
   for (int q = 0; q < LW; ++q) {
-    const int f = wave + q * NWAVE;
+    const int f = min(wave + q * NWAVE, F - 1);
     const bool isw = f < KS * NTW;
     const int ff = isw ? f : f - KS * NTW;
     const int tile = ff / KS, kk = ff % KS;
