@@ -165,9 +165,11 @@ def main():
     committed = sum(s.committed for s in stats)
     steps = sum(s.steps for s in stats)
     refresh_ms = sum(s.ms_refresh for s in stats)
-    # every DualCache/PrefixCache refresh recomputes the whole canvas, so the
-    # first (prompt) refresh of a decode costs ms_refresh / refreshes
-    first_refresh_ms = sum(s.ms_refresh / max(s.refreshes, 1) for s in stats)
+    # under DualCache/PrefixCache the decode runs every refresh as the forward
+    # of the step after it: those steps count as steps and their time as
+    # refresh time, so the time per step from the cache leaves them out
+    cached = w.cache in ("dual", "prefix")
+    cache_steps = steps - sum(s.refreshes for s in stats) if cached else steps
     dtype = "f16" if shape.dtype == "bf16" else "f32"
     n = max(kt["launches"], 1)
     intensity = kt["flops"] / max(kt["bytes"], 1.0)
@@ -203,7 +205,8 @@ def main():
                    "alpha_max": w.alpha_max, "weights": shape.dtype},
         "denoise_steps_per_s": steps / elapsed,
         "tokens_per_denoise_step": committed / max(steps, 1),
-        "ms_per_denoise_step": (elapsed * 1e3 - refresh_ms) / max(steps, 1),
+        "ms_per_denoise_step": (elapsed * 1e3 - refresh_ms) / max(cache_steps, 1),
+        "steps_with_refresh_per_decode": (steps - cache_steps) / args.steps,
         "ms_refresh_per_decode": refresh_ms / args.steps,
         # eq. (15) of the reading notes: S C_active + R + T_selection (device time per decode)
         "cost_split_ms_per_decode": {"steps_forward": sum(s.ms_step for s in stats) / args.steps,
@@ -211,10 +214,9 @@ def main():
                                      "selection": sum(s.ms_select for s in stats) / args.steps,
                                      "host": sum(s.ms_total - s.ms_step - s.ms_select - s.ms_refresh
                                                  for s in stats) / args.steps},
-        "value_excl_initial_refresh": committed / (elapsed - first_refresh_ms / 1e3),
         "roofline": roof,
     }
-    ms_step = (elapsed * 1e3 - refresh_ms) / max(steps, 1)
+    ms_step = (elapsed * 1e3 - refresh_ms) / max(cache_steps, 1)
     if shape.name == "llada8b" and w.batch == 1 and w.cache == "dual":
         # whole denoising step against HBM: weights (layers + LM head) read once,
         # the canvas's K/V read, the block's K/V written

@@ -774,10 +774,12 @@ dllm_status eval_block(dllm_ctx* c, const dllm_canvas* cv, const dllm_decode_cfg
 
 // ev (optional): three events recorded before the forward, after the LM-head
 // projection and after select/commit (the forward / selection split of a step).
+// eval_cache: the cache mode whose rows the forward recomputes (d->cache when
+// negative).
 template <typename T>
 dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, int j, int* n_committed,
                       int* block_done, float* dbg_logits, float* dbg_conf, int* dbg_tok, const StepWs& ws,
-                      hipEvent_t* ev = nullptr) {
+                      hipEvent_t* ev = nullptr, int eval_cache = -1) {
   const dllm_model_cfg& m = c->cfg;
   if (j < 0 || j >= d->gen_len / d->block_len) return fail(DLLM_ERR_ARG, "block_idx out of range");
   if ((cv->bias_target == nullptr) != (cv->bias_alpha == nullptr))
@@ -785,7 +787,7 @@ dllm_status step_impl(dllm_ctx* c, dllm_canvas* cv, const dllm_decode_cfg* d, in
   const int s = d->prompt_len + j * d->block_len;
   const int B = d->block_len, HR = d->batch * B;
   if (ev) HIPCHK(hipEventRecord(ev[0], c->stream));
-  TRY(eval_block<T>(c, cv, d, j, d->cache, dbg_logits, ws, ev ? ev[1] : nullptr));
+  TRY(eval_block<T>(c, cv, d, j, eval_cache < 0 ? d->cache : eval_cache, dbg_logits, ws, ev ? ev[1] : nullptr));
   Fwd f = make_fwd(c, cv, d);
   SelectArgs sa{};
   sa.tokens = cv->tokens;
@@ -1275,19 +1277,38 @@ void dllm_set_device_limit(uint64_t bytes) { g_device_limit.store(bytes); }
 }  // extern "C"
 
 namespace {
+// with_refresh (PREFIX / DUAL): the step whose forward is the cache pass.
+// Its forward recomputes every row of the canvas, which writes every layer's
+// K/V exactly as dllm_refresh_cache does, and its logits at the block rows are
+// those of a step from that fresh cache ([RN] sec. 3: right after a refresh
+// the cached step is exact), so refresh + step take one full forward instead
+// of a full and a block forward.  Its kernels are timed with the cache passes.
 dllm_status block_step(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cfg* cfg, int32_t block_idx,
                        int32_t* n_committed, int32_t* block_done, float* dbg_logits, float* dbg_conf, int32_t* dbg_tok,
-                       hipEvent_t* ev, const StepWs* ws_in = nullptr) {
+                       hipEvent_t* ev, const StepWs* ws_in = nullptr, bool with_refresh = false) {
   g_err.clear();
-  const Range range("dllm_block_step");
+  const Range range(with_refresh ? "dllm_block_step (cache pass)" : "dllm_block_step");
   if (!ctx || !canvas || !canvas->tokens) return fail(DLLM_ERR_ARG, "ctx, canvas and canvas->tokens must be non-NULL");
   TRY(validate_decode(ctx, cfg));
   if ((dbg_conf == nullptr) != (dbg_tok == nullptr)) return fail(DLLM_ERR_ARG, "dbg_conf and dbg_tok must both be set or both NULL");
   if (block_idx < 0 || block_idx >= cfg->gen_len / cfg->block_len) return fail(DLLM_ERR_ARG, "block_idx out of range");
-  TRY(check_cache_ready(ctx, cfg, "dllm_block_step"));
+  if (with_refresh && cfg->cache != DLLM_CACHE_PREFIX && cfg->cache != DLLM_CACHE_DUAL)
+    return fail(DLLM_ERR_ARG, "internal: a refreshing step needs PREFIX or DUAL");
+  if (!with_refresh) TRY(check_cache_ready(ctx, cfg, "dllm_block_step"));
   const StepWs ws = ws_in ? *ws_in : ctx_ws(ctx);
-  return ctx->bf16 ? step_impl<f16_t>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok, ws, ev)
-                   : step_impl<float>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok, ws, ev);
+  const int ec = with_refresh ? (int)DLLM_CACHE_NONE : -1;
+  if (with_refresh) ctx->timing_slot = DLLM_K_COUNT;
+  const dllm_status s =
+      ctx->bf16 ? step_impl<f16_t>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok, ws, ev, ec)
+                : step_impl<float>(ctx, canvas, cfg, block_idx, n_committed, block_done, dbg_logits, dbg_conf, dbg_tok, ws, ev, ec);
+  ctx->timing_slot = 0;
+  if (s == DLLM_OK && with_refresh) {
+    ctx->cache_ready = true;
+    ctx->ready_batch = cfg->batch;
+    ctx->ready_prompt = cfg->prompt_len;
+    ctx->ready_gen = cfg->gen_len;
+  }
+  return s;
 }
 
 // HIP events owned for the duration of one call
@@ -1426,31 +1447,34 @@ dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cf
   TRY(tr.open());
 
   // e[0], e[1]: around a cache pass; e[2..4]: a step's forward / selection
-  // split, taken on every kSplitEvery-th step only (each event pair lengthens
-  // the launch gaps around it by microseconds) and scaled to all steps
+  // split, taken on every kSplitEvery-th step that is not a cache pass only
+  // (each event pair lengthens the launch gaps around it by microseconds) and
+  // scaled to all such steps
   constexpr int64_t kSplitEvery = 8;
   Events ev;
   TRY(ev.create());
   double ms_refresh = 0.0, ms_step = 0.0, ms_select = 0.0;
-  int64_t split_steps = 0;
+  int64_t split_steps = 0, plain_steps = 0;
   int64_t steps = 0, refreshes = 0, committed = 0;
   std::vector<int> nc(cfg->batch), done(cfg->batch), was_done(cfg->batch), masked(cfg->batch);
   std::vector<int64_t> seq_steps(cfg->batch, 0);
   const bool steps_rule = cfg->rule == DLLM_RULE_STEPS;
   const int max_in_block = steps_rule ? cfg->k : cfg->block_len;
   // block: the answer block being decoded (-1 before the first)
+  auto refresh_done = [&](int blk, int block, int in_block, double ms) {
+    ms_refresh += ms;
+    ++refreshes;
+    if (tr.f)
+      std::fprintf(tr.f, "{\"event\":\"refresh\",\"block\":%d,\"in_block\":%d,\"pass\":%d,\"ms\":%.4f}\n",
+                   block, in_block, blk, ms);
+  };
   auto timed_refresh = [&](int blk, int block, int in_block) -> dllm_status {
     HIPCHK(hipEventRecord(ev.e[0], ctx->stream));
     TRY(dllm_refresh_cache(ctx, canvas, cfg, blk));
     HIPCHK(hipEventRecord(ev.e[1], ctx->stream));
     HIPCHK(hipEventSynchronize(ev.e[1]));
     dllm_status es = DLLM_OK;
-    const double ms = ev.ms(0, 1, &es);
-    ms_refresh += ms;
-    ++refreshes;
-    if (tr.f)
-      std::fprintf(tr.f, "{\"event\":\"refresh\",\"block\":%d,\"in_block\":%d,\"pass\":%d,\"ms\":%.4f}\n",
-                   block, in_block, blk, ms);
+    refresh_done(blk, block, in_block, ev.ms(0, 1, &es));
     return es;
   };
   dllm_status st = DLLM_OK;
@@ -1460,39 +1484,48 @@ dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cf
   if (bc) st = timed_refresh(-1, -1, 0);
   for (int j = 0; st == DLLM_OK && j < nb; ++j) {
     const Range block_range("block %d", j);
-    if (cached) st = timed_refresh(0, j, 0);
     int in_block = 0;
     std::fill(was_done.begin(), was_done.end(), 0);
     // at most block_len rows of each sequence are masked when a block begins
     std::fill(masked.begin(), masked.end(), cfg->block_len);
     while (st == DLLM_OK) {
-      if (cached && cfg->refresh_every > 0 && in_block > 0 && in_block % cfg->refresh_every == 0) {
-        st = timed_refresh(0, j, in_block);
-        if (st != DLLM_OK) break;
-      }
-      hipEvent_t* step_ev = (stats && steps % kSplitEvery == 0) ? ev.e + 2 : nullptr;
+      // PREFIX / DUAL: the refresh at the block's start (and every
+      // refresh_every steps) is the forward of the step that follows it
+      const bool with_refresh =
+          cached && (in_block == 0 || (cfg->refresh_every > 0 && in_block % cfg->refresh_every == 0));
+      hipEvent_t* step_ev = with_refresh || (stats && plain_steps % kSplitEvery == 0) ? ev.e + 2 : nullptr;
       int bound = 0;
       for (int b = 0; b < cfg->batch; ++b) bound += masked[b];
       ctx->head_rows_hint = bound;
-      st = block_step(ctx, canvas, cfg, j, nc.data(), done.data(), nullptr, nullptr, nullptr, step_ev);
+      st = block_step(ctx, canvas, cfg, j, nc.data(), done.data(), nullptr, nullptr, nullptr, step_ev, nullptr,
+                      with_refresh);
       ctx->head_rows_hint = -1;
       if (st != DLLM_OK) break;
       for (int b = 0; b < cfg->batch; ++b) masked[b] = done[b] ? 0 : std::max(0, masked[b] - nc[b]);
       double ms_fwd = -1.0, ms_sel = -1.0;
-      if (step_ev) {   // the step returned after its status readback: the events are complete
-        ms_fwd = ev.ms(2, 3, &st);
-        ms_sel = ev.ms(3, 4, &st);
-        ms_step += ms_fwd;
-        ms_select += ms_sel;
-        ++split_steps;
+      if (with_refresh) {
+        // the whole pass (forward, LM head, selection) counts as the refresh;
+        // the step returned after its status readback: the events are complete
+        refresh_done(0, j, in_block, ev.ms(2, 4, &st));
         if (st != DLLM_OK) break;
+      } else {
+        if (step_ev) {
+          ms_fwd = ev.ms(2, 3, &st);
+          ms_sel = ev.ms(3, 4, &st);
+          ms_step += ms_fwd;
+          ms_select += ms_sel;
+          ++split_steps;
+          if (st != DLLM_OK) break;
+        }
+        ++plain_steps;
       }
       if (tr.f) {
         std::fprintf(tr.f, "{\"event\":\"step\",\"block\":%d,\"in_block\":%d,\"step\":%lld", j, in_block,
                      (long long)steps);
         tr.list("committed", nc, cfg->batch);
         tr.list("done", done, cfg->batch);
-        if (step_ev) std::fprintf(tr.f, ",\"ms_forward\":%.4f,\"ms_select\":%.4f", ms_fwd, ms_sel);
+        if (with_refresh) std::fputs(",\"cache_pass\":1", tr.f);
+        if (ms_fwd >= 0.0) std::fprintf(tr.f, ",\"ms_forward\":%.4f,\"ms_select\":%.4f", ms_fwd, ms_sel);
         std::fputs("}\n", tr.f);
       }
       ++steps;
@@ -1528,7 +1561,7 @@ dllm_status dllm_decode(dllm_ctx* ctx, dllm_canvas* canvas, const dllm_decode_cf
     for (int64_t v : seq_steps) mx = v > mx ? v : mx;
     stats->max_seq_steps = mx;
     stats->ms_refresh = ms_refresh;
-    const double scale = split_steps ? (double)steps / (double)split_steps : 0.0;
+    const double scale = split_steps ? (double)plain_steps / (double)split_steps : 0.0;
     stats->ms_step = ms_step * scale;
     stats->ms_select = ms_select * scale;
     stats->ms_total = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();

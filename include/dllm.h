@@ -168,9 +168,13 @@ typedef struct {
  *              confidence) and applying the rule (merge + select/commit);
  * each the device time between HIP events on the context's stream: every
  * cache pass is timed; the step split is timed on every 8th denoising step
- * (the 1st, 9th, ...) and scaled to all steps, since each event lengthens the
- * launch gaps around it by microseconds.  ms_total - (ms_step + ms_refresh +
- * ms_select) is host time: launches and the per-step status readback. */
+ * that is not a cache pass (the 1st, 9th, ...) and scaled to all of them,
+ * since each event lengthens the launch gaps around it by microseconds.
+ * Under PREFIX and DUAL, dllm_decode makes each refresh the forward of the
+ * step that follows it (see dllm_decode): such a step counts in steps and in
+ * refreshes, and all of its device time (forward, LM head, selection) in
+ * ms_refresh.  ms_total - (ms_step + ms_refresh + ms_select) is host time:
+ * launches and the per-step status readback. */
 typedef struct {
   int64_t steps;          /* denoising steps (forward passes with a commit)   */
   int64_t refreshes;      /* full-canvas K/V refresh passes                   */
@@ -178,8 +182,8 @@ typedef struct {
   int64_t max_seq_steps;  /* largest per-sequence step count                  */
   double ms_total;        /* wall time of the call                            */
   double ms_refresh;      /* device time in refresh / prefill / commit passes */
-  double ms_step;         /* device time in the steps' forward passes         */
-  double ms_select;       /* device time in LM-head merge + select/commit     */
+  double ms_step;         /* device time in the other steps' forward passes   */
+  double ms_select;       /* device time in their LM-head merge + selection   */
 } dllm_stats;
 
 typedef struct dllm_ctx dllm_ctx;
@@ -298,12 +302,20 @@ dllm_status dllm_begin_decode(dllm_ctx* ctx, const dllm_canvas* canvas, const dl
  * dllm_begin_decode, then for each block: refresh (PREFIX / DUAL) and steps until the
  * block holds no mask in any sequence (lock-step over the batch; finished
  * sequences commit nothing).  No refresh follows the last block.
+ * A refresh and the step after it share one forward: the step evaluates the
+ * block from a forward over the whole canvas, which rewrites every cached K/V
+ * exactly as dllm_refresh_cache does, and right after a refresh the cached
+ * step is exact ([RN] sec. 3), so its logits are the ones the refresh +
+ * dllm_block_step sequence computes, without the second forward over the
+ * block.  The same holds for the refreshes that refresh_every inserts.
  *   stats: host output or NULL.
  * Tracing: with the environment variable DLLM_TRACE set to a path, one JSON
  *   line is appended there per cache pass ({"event":"refresh", block,
- *   in_block, pass = block_idx given to dllm_refresh_cache, ms}), per step
- *   ({"event":"step", block, in_block, step, committed[batch], done[batch],
- *   and on every 8th step ms_forward / ms_select}) and per decode
+ *   in_block, pass = block_idx given to dllm_refresh_cache (0 for the
+ *   PREFIX / DUAL refreshes), ms}), per step ({"event":"step", block,
+ *   in_block, step, committed[batch], done[batch], cache_pass = 1 on a step
+ *   that refreshed the cache (its refresh line comes first), and on every
+ *   8th other step ms_forward / ms_select}) and per decode
  *   ({"event":"decode", steps, refreshes, committed}).  dllm_decode, each
  *   block, dllm_refresh_cache and dllm_block_step push roctx ranges
  *   (rocprofv3 --marker-trace).

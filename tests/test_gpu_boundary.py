@@ -131,9 +131,10 @@ def test_stats_split_device_time(eng32):
     pr, t, a = _inputs()
     cv = eng32.canvas(pr, t, a, 64)
     st = eng32.decode(cv, Engine.decode_cfg(1, 32, 64, 16))
+    # each block's first step is its refresh pass; the others split the time
+    assert st.refreshes == 4 and st.committed == 64 and st.steps > st.refreshes
     assert st.ms_step > 0 and st.ms_select > 0 and st.ms_refresh > 0
     assert st.ms_step + st.ms_select + st.ms_refresh <= st.ms_total
-    assert st.refreshes == 4 and st.committed == 64
 
 
 def test_trace_log_matches_stats(eng32, tmp_path, monkeypatch):
@@ -159,7 +160,17 @@ def test_trace_log_matches_stats(eng32, tmp_path, monkeypatch):
         assert [x["in_block"] for x in blk] == list(range(len(blk)))
         assert blk[-1]["done"] == [1, 1]
         assert sum(sum(x["committed"]) for x in blk) == 2 * 16
-    assert all(("ms_forward" in x) == (x["step"] % 8 == 0) for x in steps)
+    # each block's first step is a cache pass, logged right after its refresh
+    # line; the forward / selection split is sampled on every 8th other step
+    passes = [x for x in steps if x.get("cache_pass")]
+    assert [(x["block"], x["in_block"]) for x in passes] == [(j, 0) for j in range(4)]
+    for i, x in enumerate(lines):
+        if x.get("cache_pass"):
+            assert lines[i - 1]["event"] == "refresh"
+            assert (lines[i - 1]["block"], lines[i - 1]["in_block"]) == (x["block"], x["in_block"])
+    plain = [x for x in steps if not x.get("cache_pass")]
+    assert plain and all(("ms_forward" in x) == (k % 8 == 0) for k, x in enumerate(plain))
+    assert not any("ms_forward" in x for x in passes)
     assert all(x["ms"] > 0 for x in refreshes)
     monkeypatch.setenv("DLLM_TRACE", str(tmp_path / "no_such_dir" / "trace.jsonl"))
     cv = eng32.canvas(pr, t, a, 64)

@@ -165,6 +165,40 @@ def test_refresh_every_full_decode_matches_oracle(engines, cache, r):
     assert o1.refreshes > 4             # the interval fired inside blocks
 
 
+@pytest.mark.parametrize("cache,r", [("dual", 0), ("prefix", 0), ("dual", 3), ("prefix", 5)])
+def test_decode_shares_refresh_and_step_forward(engines, cache, r):
+    """dllm_decode evaluates the step after each refresh from the refresh's
+    own forward over the whole canvas; a loop driven through
+    dllm_refresh_cache + dllm_block_step (a second forward, over the block or
+    the suffix) commits the same tokens at the same steps (fp32), with the
+    same step and refresh counts."""
+    from diffusion_lm_decoding_amd.engine import Engine
+    eng, _ = engines["f32"]
+    pr, t, a = _inputs(2, 32, 64, seed=91 + r, alpha_max=16.0)
+    cfg = Engine.decode_cfg(2, 32, 64, 16, cache=cache, refresh_every=r)
+    c1 = eng.canvas(pr, t, a, 64)
+    st = eng.decode(c1, cfg)
+    c2 = eng.canvas(pr, t, a, 64)
+    eng.begin(c2, cfg)
+    steps = refreshes = 0
+    for j in range(4):
+        n = 0
+        while True:
+            if n == 0 or (r and n % r == 0):
+                eng.refresh(c2, cfg, 0)
+                refreshes += 1
+            _, done, *_ = eng.step(c2, cfg, j)
+            steps += 1
+            n += 1
+            if np.asarray(done).all():
+                break
+            assert n < 16, "block outlived its step bound"
+    assert np.array_equal(c1.tokens.cpu().numpy(), c2.tokens.cpu().numpy())
+    assert np.array_equal(c1.commit_step.cpu().numpy(), c2.commit_step.cpu().numpy())
+    assert st.steps == steps and st.refreshes == refreshes
+    assert steps > refreshes            # steps from the cache ran too
+
+
 @pytest.mark.parametrize("cache", ["dual", "prefix"])
 @pytest.mark.parametrize("r", [2, 4])
 def test_refresh_every_lockstep_f32(engines, cache, r):
