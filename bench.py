@@ -2,7 +2,8 @@
 MI355X (LLaDA-8B-shaped random model, DualCache, block 32, tau 0.9).
 
 One timed "step" is one whole dllm_decode of the workload: every block's
-cache refresh, every denoising step (block forward, LM-head reduce,
+cache refresh (whose whole-canvas forward also evaluates the block's first
+denoising step), every other denoising step (block forward, LM-head reduce,
 select/commit) and the per-step readback.  Inputs (weights, prompt, planted
 bias) are synthetic and already resident in HBM when timing starts.
 
