@@ -126,8 +126,7 @@ struct dllm_ctx {
   float* g_final = nullptr;
   std::vector<void*> wqkv, wo, wgu, wd;
   void* wlm = nullptr;
-  float* rope_cos = nullptr;
-  float* rope_sin = nullptr;
+  float* rope = nullptr;      // [seq_pad][head_dim/4][4], see EpiQKV::rot
   void* kc = nullptr;
   void* vt = nullptr;
   size_t kv_layer = 0;  // elements per layer
@@ -666,7 +665,7 @@ dllm_status forward(dllm_ctx* c, const Fwd& f) {
   for (int l = 0; l < m.n_layers; ++l) {
     EpiQKV<T> eq{g, d, m.head_dim, m.n_heads, c->seq_pad, static_cast<T*>(c->q),
                  static_cast<T*>(c->kc) + (size_t)l * c->kv_layer, static_cast<T*>(c->vt) + (size_t)l * c->kv_layer,
-                 c->rope_cos, c->rope_sin};
+                 c->rope};
     TRY(launch_gemm<T>(c, DLLM_K_QKV, c->xin, c->wqkv[l], M, 3 * d, d, eq, c->ssq, M));
     if (f.kv_only && l == m.n_layers - 1) break;
     TRY(attention<T>(c, l, f));
@@ -959,19 +958,20 @@ dllm_status init_impl(dllm_ctx* c, const void* const* t) {
   TRY(c->alloc(&c->wlm, (size_t)V * d * es));
   TRY(pack<T>(c, t[2 + 9 * L], nullptr, V, d, 0, c->wlm, 0));
 
-  // rotary tables: angle = pos * theta^(-2j/dh), computed in double
+  // rotary table: angle of pair j at position pos = pos * theta^(-2j/dh),
+  // computed in double; entry (pos, j) at pos * dh + 4 * (j / 2) + 2 * (j % 2)
+  // (cos) and one further (sin)
   const int half = dh / 2;
-  std::vector<float> cs((size_t)c->seq_pad * half), sn((size_t)c->seq_pad * half);
+  std::vector<float> rot((size_t)c->seq_pad * dh);
   for (int pos = 0; pos < c->seq_pad; ++pos)
     for (int j = 0; j < half; ++j) {
       const double ang = (double)pos * std::pow((double)m.rope_theta, -2.0 * j / dh);
-      cs[(size_t)pos * half + j] = (float)std::cos(ang);
-      sn[(size_t)pos * half + j] = (float)std::sin(ang);
+      const size_t o = (size_t)pos * dh + 4 * (j / 2) + 2 * (j % 2);
+      rot[o] = (float)std::cos(ang);
+      rot[o + 1] = (float)std::sin(ang);
     }
-  TRY(c->alloc(&c->rope_cos, cs.size() * sizeof(float)));
-  TRY(c->alloc(&c->rope_sin, sn.size() * sizeof(float)));
-  HIPCHK(hipMemcpyAsync(c->rope_cos, cs.data(), cs.size() * sizeof(float), hipMemcpyHostToDevice, c->stream));
-  HIPCHK(hipMemcpyAsync(c->rope_sin, sn.data(), sn.size() * sizeof(float), hipMemcpyHostToDevice, c->stream));
+  TRY(c->alloc(&c->rope, rot.size() * sizeof(float)));
+  HIPCHK(hipMemcpyAsync(c->rope, rot.data(), rot.size() * sizeof(float), hipMemcpyHostToDevice, c->stream));
 
   // KV cache (zeroed: keys past the canvas are masked but must be finite)
   c->kv_layer = (size_t)m.max_batch * m.n_heads * c->seq_pad * dh;

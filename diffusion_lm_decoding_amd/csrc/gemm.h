@@ -71,8 +71,12 @@ struct EpiQKV {
   T* q;             // [rows][d], per-head rotary pair order
   T* kc;            // [batch][H][seq_pad][dh], rotary pair order
   T* vt;            // [batch][H][dh][seq_pad], key order vt_col
-  const float* cs;  // [seq][dh/2] cos
-  const float* sn;  // [seq][dh/2] sin
+  // [seq][dh/4][4]: cos, sin of rotary pair 2g, then of pair 2g+1, so a
+  // lane's two pairs (columns 4g .. 4g+3) take one 16-byte load and the 16
+  // rows of a tile two cache lines per position run (measured on MI355X at
+  // 512 rows against separate [seq][dh/2] cos and sin tables, four loads:
+  // 62.7 -> 58 us with 192x128 tiles, 90-91 -> 79-81 us with 192x256)
+  const float* rot;
   __device__ void operator()(int nt, int mt, const f32x4& acc, int lane) const {
     const int m = mt * 16 + (lane & 15);
     if (m >= g.M) return;
@@ -82,13 +86,14 @@ struct EpiQKV {
     float v[4] = {acc[0], acc[1], acc[2], acc[3]};
     const int region = n0 / d, nn = n0 % d, h = nn / dh, p = nn % dh;
     if (region < 2) {
+      // p % 4 == 0: pairs p/2 and p/2 + 1 are group p/4
+      const f32x4 r = *reinterpret_cast<const f32x4*>(rot + ((size_t)pos * (dh / 4) + (p >> 2)) * 4);
 #pragma unroll
-      for (int t = 0; t < 4; t += 2) {
-        const int j = (p + t) >> 1;
-        const float c = cs[pos * (dh / 2) + j], s = sn[pos * (dh / 2) + j];
-        const float e = v[t], o = v[t + 1];
-        v[t] = e * c - o * s;
-        v[t + 1] = o * c + e * s;
+      for (int t = 0; t < 2; ++t) {
+        const float c = r[2 * t], s = r[2 * t + 1];
+        const float e = v[2 * t], o = v[2 * t + 1];
+        v[2 * t] = e * c - o * s;
+        v[2 * t + 1] = o * c + e * s;
       }
       T* dst = region == 0 ? q + (size_t)m * d + nn : kc + (((size_t)b * H + h) * seq_pad + pos) * dh + p;
       store_run<T, 4>(dst, v);
